@@ -1,0 +1,315 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic inputs:
+  1. fa_fwd on the GPT-2-medium-shaped prefill: B=64, H=16, N=Nk=1024,
+     d=dv=64, bf16, causal (inputs 0.5*N(0,1));
+  2. fa_decode_splitkv on the long-context decode: B=8, H=32, N=1,
+     Nk=32768, d=dv=128, bf16, 64 splits (segment kernel + merge kernel).
+
+Inputs are drawn on the GPU with seeded generators before timing starts.
+Every launch is bracketed by HIP events recorded on the stream the library
+launches on (torch's current stream), so per-kernel times are live device
+times.  ``value`` is the prefill throughput in TFLOP/s, crediting
+4*N*Nk*d per head, halved for the causal mask (sum of credited FLOPs over
+the timed steps / sum of the prefill launch times).  The decode figures
+(HBM GB/s over K+V+Q+O+LSE bytes) are reported beside it.
+
+The CPU baseline is the FP64 oracle (test infrastructure) timed on a bounded
+sample of the prefill workload on the host cores, in the same run.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --summarize-pmc DIR   (turn rocprofv3 --pmc CSVs into
+                                              the traffic summary under profiles/)
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); split-KV decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0          # HBM3E
+PREFILL = "prefill_b64_h16_n1024_d64"
+DECODE = "decode_b8_h32_nk32768_d128"
+FWD_KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc",
+                              "fa_fwd_mfma.hip")
+DEC_KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc",
+                              "fa_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+COPY_BYTES = 1 << 30           # plain copy used to calibrate the traffic counters
+
+
+def credited_flops(s, causal: bool) -> float:
+    per_head = 4.0 * s.N * s.Nk * s.d
+    if causal:
+        per_head /= 2
+    return per_head * s.B * s.H
+
+
+def decode_bytes(s) -> int:
+    """Algorithmic bytes of one decode call: K and V once, Q, O (bf16), LSE (fp32)."""
+    e = 2
+    return (s.B * s.H * (2 * s.Nk * s.d * e + s.N * s.d * e + s.N * s.dv * e + s.N * 4))
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """Per-launch HBM traffic from the committed counter summary, or None per
+    kernel if absent or if that kernel's source changed since it was taken."""
+    out = {"fwd": None, "decode": None}
+    if not os.path.exists(TRAFFIC_FILE):
+        return out
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+    try:
+        if kv.get("fwd_source_sha256_16") == source_hash(FWD_KERNEL_SRC):
+            out["fwd"] = float(kv["fwd_bytes_per_launch"])
+        if kv.get("decode_source_sha256_16") == source_hash(DEC_KERNEL_SRC):
+            out["decode"] = float(kv["decode_bytes_per_launch"])
+    except (KeyError, ValueError):
+        pass
+    return out
+
+
+def cpu_baseline(q, k, v, s, causal, heads: int):
+    """The FP64 oracle on the first ``heads`` heads of the prefill inputs."""
+    import oracle
+    import synth_inputs as si
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    qb = q.reshape(-1, s.N, s.d)[:heads]
+    kb = k.reshape(-1, s.Nk, s.d)[:heads]
+    vb = v.reshape(-1, s.Nk, s.dv)[:heads]
+    qf, kf, vf = si.as_f64(qb), si.as_f64(kb), si.as_f64(vb)
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    orc.attention(qf, kf, vf, causal=causal, scale=1.0 / math.sqrt(s.d), nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = credited_flops(s, causal) * heads / (s.B * s.H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {s.B * s.H} heads of {PREFILL} (FP64 standard attention, "
+                      f"{flops / 1e9:.1f} GFLOP credited, {dt:.2f} s wall on {threads} threads)"}
+
+
+def summarize_pmc(directory: str) -> None:
+    """Build profiles/traffic_counters.txt from two rocprofv3 --pmc runs
+    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) that include the 1 GiB
+    calibration copy; the copy's counters give the KiB->byte scale."""
+    import csv
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+
+    def per_kernel(counter, pred):
+        vals = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and pred(r["Kernel_Name"])]
+        return sum(vals) / len(vals) if vals else None
+
+    is_fwd = lambda n: "fwd_mfma_kernel" in n
+    is_seg = lambda n: "decode_segment_kernel" in n
+    is_merge = lambda n: "decode_merge_kernel" in n
+    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and "fa" not in n[:3]
+    out = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = per_kernel(counter, is_copy)
+        if cp is None:
+            raise SystemExit(f"no calibration copy kernel found for {counter}")
+        scale = COPY_BYTES / (cp * 1024.0)   # bytes per counted KiB-unit... for the copy
+        out[counter] = {"copy_kib": cp, "scale": scale,
+                        "fwd_kib": per_kernel(counter, is_fwd),
+                        "seg_kib": per_kernel(counter, is_seg),
+                        "merge_kib": per_kernel(counter, is_merge)}
+    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    fwd_b = (fetch["fwd_kib"] * 1024 * fetch["scale"] + write["fwd_kib"] * 1024 * write["scale"])
+    dec_b = ((fetch["seg_kib"] + fetch["merge_kib"]) * 1024 * fetch["scale"]
+             + (write["seg_kib"] + write["merge_kib"]) * 1024 * write["scale"])
+    lines = [
+        "# HBM traffic per launch from rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE, KiB per",
+        "# dispatch, averaged over dispatches), each scaled so that a plain 1 GiB device copy",
+        "# reads and writes exactly 1 GiB.  Made by: python bench.py --summarize-pmc <dir>.",
+        f"copy_fetch_kib: {fetch['copy_kib']:.1f}",
+        f"copy_write_kib: {write['copy_kib']:.1f}",
+        f"fetch_scale: {fetch['scale']:.6f}",
+        f"write_scale: {write['scale']:.6f}",
+        f"fwd_fetch_kib: {fetch['fwd_kib']:.1f}",
+        f"fwd_write_kib: {write['fwd_kib']:.1f}",
+        f"fwd_bytes_per_launch: {fwd_b:.0f}",
+        f"fwd_source_sha256_16: {source_hash(FWD_KERNEL_SRC)}",
+        f"decode_segment_fetch_kib: {fetch['seg_kib']:.1f}",
+        f"decode_segment_write_kib: {write['seg_kib']:.1f}",
+        f"decode_merge_fetch_kib: {fetch['merge_kib']:.1f}",
+        f"decode_merge_write_kib: {write['merge_kib']:.1f}",
+        f"decode_bytes_per_launch: {dec_b:.0f}",
+        f"decode_source_sha256_16: {source_hash(DEC_KERNEL_SRC)}",
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=256,
+                    help="prefill heads the CPU oracle is timed on")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="add one plain 1 GiB device copy per step (for counter calibration)")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the attention path shards heads or key ranges with no collective on the hot "
+              "path; this benchmark measures one GPU's share).", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_tiled_attention_flashattention_amd as fa
+    import synth_inputs as si
+
+    fa.library()   # fail loudly here if the HIP library is missing
+    dev = torch.device("cuda:0")
+    wp = si.WORKLOADS[PREFILL]
+    wd = si.WORKLOADS[DECODE]
+    sp, sd = wp.shapes[0], wd.shapes[0]
+    print(f"# drawing inputs: {wp.description}; {wd.description}", file=sys.stderr, flush=True)
+    qp, kp, vp = si.device_qkv(sp, wp.seed, wp.dtype, dev, wp.std)
+    qd, kd, vd = si.device_qkv(sd, wd.seed, wd.dtype, dev, wd.std)
+    op = torch.empty((sp.B, sp.H, sp.N, sp.dv), dtype=qp.dtype, device=dev)
+    lp = torch.empty((sp.B, sp.H, sp.N), dtype=torch.float32, device=dev)
+    od = torch.empty((sd.B, sd.H, sd.N, sd.dv), dtype=qd.dtype, device=dev)
+    ld = torch.empty((sd.B, sd.H, sd.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_splitkv_workspace_size(sd.B, sd.H, sd.N, sd.dv, wd.num_splits),
+                     dtype=torch.uint8, device=dev)
+    copy_src = copy_dst = None
+    if args.calibration_copy:
+        copy_src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+    stream = torch.cuda.current_stream(dev)
+    scale_p = 1.0 / math.sqrt(sp.d)
+    scale_d = 1.0 / math.sqrt(sd.d)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(qp, kp, vp, causal=True, scale=scale_p, out=op, lse=lp)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.decode_splitkv(qd, kd, vd, causal=False, scale=scale_d, num_splits=wd.num_splits,
+                          workspace=ws, out=od, lse=ld)
+        if ev is not None:
+            ev[2].record(stream)
+        if copy_src is not None:
+            copy_dst.copy_(copy_src)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    assert torch.isfinite(lp).all().item() and torch.isfinite(ld).all().item()
+
+    flops = credited_flops(sp, True)
+    fwd_avg_s = sum(fwd_ms) / len(fwd_ms) / 1e3
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    tflops = flops / fwd_avg_s / 1e12
+    dbytes = decode_bytes(sd)
+    dec_gbs = dbytes / dec_avg_s / 1e9
+    traffic = read_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded torch Philox draws on the GPU)",
+        "config": {
+            "workload": f"{PREFILL} (fa_fwd) + {DECODE} (fa_decode_splitkv)",
+            "prefill": {"B": sp.B, "H": sp.H, "N": sp.N, "Nk": sp.Nk, "d": sp.d, "causal": True,
+                        "input_std": wp.std},
+            "decode": {"B": sd.B, "H": sd.H, "N": sd.N, "Nk": sd.Nk, "d": sd.d,
+                       "num_splits": wd.num_splits},
+        },
+        "roofline": {
+            "kernel": "fwd_mfma_kernel<bf16,64,causal>",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic["fwd"],
+            "avg_launch_us": round(fwd_avg_s * 1e6, 2),
+            "min_launch_us": round(min(fwd_ms) * 1e3, 2),
+            "credited_flop_per_launch": flops,
+        },
+        "decode": {
+            "metric": "split-KV decode HBM GB/s",
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "roofline": {
+                "kernel": "decode_segment_kernel<bf16,128,1> + decode_merge_kernel",
+                "bound": "hbm",
+                "achieved": round(dec_gbs, 1),
+                "peak": PEAK_HBM_GBS,
+                "unit": "GB/s",
+                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic["decode"],
+                "avg_launch_us": round(dec_avg_s * 1e6, 2),
+                "min_launch_us": round(min(dec_ms) * 1e3, 2),
+                "algorithmic_bytes_per_launch": dbytes,
+            },
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(qp, kp, vp, sp, True, min(args.cpu_heads, sp.B * sp.H))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,153 @@
+"""Exact tiled attention (FlashAttention forward + split-KV flash-decoding)
+for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libfa.so``, whose C ABI is declared in
+``include/fa.h``.  This module only marshals arguments: it checks tensor
+shapes and dtypes, allocates the outputs (and the decode workspace) with
+torch on the inputs' device, and passes raw device pointers and the current
+torch stream to the library.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "fwd", "decode_splitkv", "decode_splitkv_workspace_size", "status_string",
+    "FAError", "library", "LIBRARY_PATH", "FA_OK", "FA_ERR_INVALID_ARG",
+    "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
+]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = range(5)
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-OK status returned by libfa.so."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """The loaded ``libfa.so`` with its C signatures declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise FileNotFoundError(
+            f"{LIBRARY_PATH} is not built; run "
+            "`python -m exact_tiled_attention_flashattention_amd.build` first")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, c_int,
+                           ctypes.c_float, c_int, vp]
+    lib.fa_fwd.restype = c_int
+    lib.fa_decode_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, c_int]
+    lib.fa_decode_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, c_int,
+                                      ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_decode_splitkv.restype = c_int
+    lib.fa_status_string.argtypes = [c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().fa_status_string(int(status)).decode()
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, rows, dim], got {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must live on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q, k, v must share one dtype among float32, float16, bfloat16")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    B, H, N, d = q.shape
+    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != d or v.shape[2] != k.shape[2]:
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    return B, H, N, k.shape[2], d, v.shape[3]
+
+
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: float | None = None, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Exact attention forward through ``fa_fwd``.
+
+    q [B,H,N,d], k [B,H,Nk,d], v [B,H,Nk,dv] contiguous on one GPU, one dtype.
+    Returns ``(o, lse)``: o [B,H,N,dv] in the input dtype, lse [B,H,N] float32.
+    ``scale`` defaults to 1/sqrt(d).  The call is asynchronous on ``stream``
+    (default: torch's current stream).
+    """
+    B, H, N, Nk, d, dv = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, Nk, d, dv, int(bool(causal)), float(scale),
+                          _DTYPE_CODE[q.dtype], _stream_handle(q.device, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def decode_splitkv_workspace_size(B: int, H: int, N: int, dv: int, num_splits: int) -> int:
+    return int(library().fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits))
+
+
+def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                   scale: float | None = None, num_splits: int = 64,
+                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Split-KV flash-decoding through ``fa_decode_splitkv``.
+
+    Same inputs and result as :func:`fwd`; the keys of each head are cut into
+    ``num_splits`` segments reduced in parallel, then merged by a second kernel.
+    ``workspace`` (a uint8 device tensor of at least
+    :func:`decode_splitkv_workspace_size` bytes) is allocated if not given.
+    """
+    B, H, N, Nk, d, dv = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = decode_splitkv_workspace_size(B, H, N, dv, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = library().fa_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, N, Nk, d, dv, int(bool(causal)),
+                                     float(scale), _DTYPE_CODE[q.dtype], int(num_splits),
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream_handle(q.device, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_splitkv")
+    return out, lse

@@ -1,0 +1,151 @@
+// fa_api.cpp -- the C ABI of libfa.so (declared in include/fa.h).
+//
+// Every argument is checked before the first HIP call, so an invalid call
+// returns a status and touches nothing.  Valid calls are dispatched on
+// (dtype, d, dv) to a kernel launcher and enqueued on the caller's stream;
+// nothing is allocated and nothing is synchronised.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxI32 = std::numeric_limits<int32_t>::max();
+constexpr int kMaxSplits = 65536;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > std::numeric_limits<int64_t>::max() / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_dims(int64_t d, int64_t dv) {
+    return d == dv && (d == 32 || d == 64 || d == 128);
+}
+
+// Checks shared by both entry points.  Order: invalid arguments first, then
+// the support matrix.
+fa_status_t check_common(const void *q, const void *k, const void *v, const void *o,
+                         const float *lse, int64_t B, int64_t H, int64_t N, int64_t Nk,
+                         int64_t d, int64_t dv, float scale, fa_dtype_t dtype) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || Nk < 1 || d < 1 || dv < 1) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4))
+        return FA_ERR_INVALID_ARG;
+    // Element counts must be representable; indices inside one head are
+    // 32-bit in the kernels, and so are the workgroup counts.
+    int64_t heads, t1, t2, t3, t4, t5;
+    if (!mul_ok(B, H, &heads) || heads > kMaxI32) return FA_ERR_INVALID_ARG;
+    if (!mul_ok(N, d, &t1) || !mul_ok(Nk, d, &t2) || !mul_ok(Nk, dv, &t3) || !mul_ok(N, dv, &t4))
+        return FA_ERR_INVALID_ARG;
+    if (t1 > kMaxI32 || t2 > kMaxI32 || t3 > kMaxI32 || t4 > kMaxI32) return FA_ERR_INVALID_ARG;
+    if (!mul_ok(heads, N, &t5) || t5 > kMaxI32) return FA_ERR_INVALID_ARG;
+    int64_t total;
+    if (!mul_ok(heads, t2 > t3 ? t2 : t3, &total) || !mul_ok(heads, t1 > t4 ? t1 : t4, &total))
+        return FA_ERR_INVALID_ARG;
+    if (!supported_dims(d, dv)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa::FwdArgs make_args(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, int64_t dv,
+                      int causal, float scale, fa_dtype_t dtype, void *stream) {
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.Nk = Nk;
+    a.d = d;
+    a.dv = dv;
+    a.causal = causal ? 1 : 0;
+    a.scale = scale;
+    a.dtype = static_cast<int>(dtype);
+    a.stream = static_cast<hipStream_t>(stream);
+    return a;
+}
+
+// Keys per decode segment: ceil(Nk / S) rounded up to a multiple of 64.
+int64_t segment_length(int64_t Nk, int num_splits) {
+    int64_t per = (Nk + num_splits - 1) / num_splits;
+    return ((per + 63) / 64) * 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d, int64_t dv,
+                   int causal, float scale, fa_dtype_t dtype, void *stream) {
+    fa_status_t st = check_common(q, k, v, o, lse, B, H, N, Nk, d, dv, scale, dtype);
+    if (st != FA_OK) return st;
+    fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, stream);
+    (void)hipGetLastError();   // clear any stale error so it is not reported as ours
+    hipError_t e = fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_mfma(a)
+                                                          : fa::launch_fwd_rowwise(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t dv,
+                                        int num_splits) {
+    if (B < 1 || H < 1 || N < 1 || dv < 1 || num_splits < 1) return 0;
+    int64_t x;
+    if (!mul_ok(B, H, &x) || !mul_ok(x, num_splits, &x) || !mul_ok(x, N, &x) ||
+        !mul_ok(x, dv + 1, &x) || !mul_ok(x, 4, &x))
+        return 0;
+    if ((uint64_t)x > (uint64_t)std::numeric_limits<size_t>::max()) return 0;
+    return static_cast<size_t>(x);
+}
+
+fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d,
+                              int64_t dv, int causal, float scale, fa_dtype_t dtype,
+                              int num_splits, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    if (num_splits < 1) return FA_ERR_INVALID_ARG;
+    fa_status_t st = check_common(q, k, v, o, lse, B, H, N, Nk, d, dv, scale, dtype);
+    if (st != FA_OK) return st;
+    // Launch-shape limits of the segment kernel: (segment, head, row group).
+    if (B * H > 65535 || (N + 3) / 4 > 65535 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits);
+    if (need == 0) return FA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    fa::DecodeArgs dargs;
+    dargs.a = make_args(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, stream);
+    dargs.num_splits = num_splits;
+    dargs.seg_len = segment_length(Nk, num_splits);
+    dargs.ws_o = static_cast<float *>(workspace);
+    dargs.ws_lse = dargs.ws_o + B * H * (int64_t)num_splits * N * dv;
+    (void)hipGetLastError();
+    hipError_t e = fa::launch_decode_splitkv(dargs);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char *fa_status_string(fa_status_t status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH";
+    }
+    return "FA_UNKNOWN_STATUS";
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+// fa_decode.hip -- split-KV flash-decoding: segment kernel + merge kernel.
+//
+// Method: CS349E Lecture 11 "flash_lab.py", section 4 (split_kv_decode):
+// with only a few query rows per head there are too few query blocks to
+// fill the GPU, so the keys are cut into segments instead; each segment is
+// reduced independently to (o_s, lse_s) with o_s already normalised, and
+// the segments are combined with lse = ln sum_s e^(lse_s) and
+// o = sum_s e^(lse_s - lse) o_s -- section 1's merge_states written in
+// log-sum-exp form.  The partials go through a workspace and a second,
+// small kernel on the same stream merges them: no atomics, no inter-
+// workgroup ordering (the partial-buffer pattern the lecture series uses
+// to avoid racing writers).
+//
+// Segment kernel mapping (one workgroup of 4 waves per (segment, head, row
+// group)): a key row of D elements is read as 16-byte pieces by LPK
+// consecutive lanes (bf16/fp16 d=128: 16 lanes), so one load instruction of
+// a wave covers KPL = 64/LPK consecutive keys -- a contiguous 1 KiB of K or
+// V.  Each "key slot" (group of LPK lanes) keeps its own online-softmax
+// state (m, l, o) for every query row it serves, so the loop needs no
+// cross-slot exchange; the dot product of a key is summed over its LPK
+// lanes with DPP.  At the end the 4 waves x KPL slot states are merged
+// through LDS with the same merge rule.  The loop issues U loads of K and
+// U of V per lane before using them, to keep enough bytes in flight for
+// HBM bandwidth.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kUnroll = 4;   // loads of K (and of V) in flight per lane per step
+
+template <typename T, int D, int R>
+__global__ __launch_bounds__(kThreads) void decode_segment_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    float *__restrict__ ws_o, float *__restrict__ ws_lse, int N, int Nk, int causal,
+    float scale_log2, int num_splits, int seg_len) {
+    constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte piece
+    constexpr int LPK = D / EPL;               // lanes per key row
+    constexpr int KPL = 64 / LPK;              // keys per wave load
+    constexpr int KEYS_PER_STEP = KPL * kUnroll;
+    static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "bad key-row split");
+
+    const int split = blockIdx.x;
+    const int head = blockIdx.y;
+    const int row0 = blockIdx.z * R;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const int slot = lane / LPK;   // which key of a wave load this lane serves
+    const int t = lane % LPK;      // which 16-byte piece of the row
+
+    const T *qh = q + (int64_t)head * N * D;
+    const T *kh = k + (int64_t)head * Nk * D;
+    const T *vh = v + (int64_t)head * Nk * D;
+
+    // Query pieces of the R rows served by this workgroup (rows >= N: zero).
+    float qr[R][EPL];
+    int limit[R];   // last key index visible to each row
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int row = row0 + r;
+        const bool ok = row < N;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (ok) raw = *reinterpret_cast<const u32x4 *>(qh + (int64_t)row * D + t * EPL);
+        const T *e = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) qr[r][i] = to_f32(e[i]);
+        limit[r] = !ok ? -1 : (causal ? Nk - N + row : Nk - 1);
+    }
+
+    const int seg_begin = split * seg_len;
+    const int seg_end = min(Nk, seg_begin + seg_len);
+
+    float m[R], l[R], acc[R][EPL];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[r][i] = 0.f;
+    }
+
+    // Waves take consecutive steps of KEYS_PER_STEP keys round-robin.
+    for (int base = seg_begin + wave * KEYS_PER_STEP; base < seg_end;
+         base += kWaves * KEYS_PER_STEP) {
+        u32x4 kraw[kUnroll], vraw[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int key = base + u * KPL + slot;
+            if (key < seg_end) {
+                kraw[u] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)key * D + t * EPL);
+                vraw[u] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)key * D + t * EPL);
+            } else {
+                kraw[u] = u32x4{0u, 0u, 0u, 0u};
+                vraw[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int key = base + u * KPL + slot;
+            const T *ke = reinterpret_cast<const T *>(&kraw[u]);
+            const T *ve = reinterpret_cast<const T *>(&vraw[u]);
+            float kf[EPL], vf[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                kf[i] = to_f32(ke[i]);
+                vf[i] = to_f32(ve[i]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) part = fmaf(qr[r][i], kf[i], part);
+                const float dot = group_sum<LPK>(part);
+                const bool vis = key < seg_end && key <= limit[r];
+                const float s = vis ? dot * scale_log2 : -INFINITY;
+                // Online update of this slot's state with one key.
+                const float m_new = fmaxf(m[r], s);
+                const float alpha = (m[r] == -INFINITY) ? 0.f : fast_exp2(m[r] - m_new);
+                const float p = (s == -INFINITY) ? 0.f : fast_exp2(s - m_new);
+                l[r] = l[r] * alpha + p;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) acc[r][i] = fmaf(acc[r][i], alpha, p * vf[i]);
+                m[r] = m_new;
+            }
+        }
+    }
+
+    // Merge the kWaves * KPL slot states of every row through LDS.
+    constexpr int STATES = kWaves * KPL;
+    __shared__ float sm_m[R][STATES];
+    __shared__ float sm_l[R][STATES];
+    __shared__ float sm_o[R][STATES][D];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int st = wave * KPL + slot;
+        if (t == 0) {
+            sm_m[r][st] = m[r];
+            sm_l[r][st] = l[r];
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) sm_o[r][st][t * EPL + i] = acc[r][i];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < R * D; idx += kThreads) {
+        const int r = idx / D;
+        const int c = idx % D;
+        const int row = row0 + r;
+        if (row >= N) continue;
+        float mm = -INFINITY;
+        for (int st = 0; st < STATES; ++st) mm = fmaxf(mm, sm_m[r][st]);
+        float ll = 0.f, oo = 0.f;
+        if (mm != -INFINITY) {
+            for (int st = 0; st < STATES; ++st) {
+                const float ms = sm_m[r][st];
+                const float f = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mm);
+                ll = fmaf(sm_l[r][st], f, ll);
+                oo = fmaf(sm_o[r][st][c], f, oo);
+            }
+        }
+        // Workspace layout: o_s [B*H, S, N, D], lse_s [B*H, S, N].
+        const int64_t part = ((int64_t)head * num_splits + split) * N + row;
+        ws_o[part * D + c] = ll > 0.f ? oo / ll : 0.f;
+        if (c == 0) ws_lse[part] = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
+    }
+}
+
+// One wave per (head, row): merge num_splits partial states.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restrict__ ws_o,
+                                                          const float *__restrict__ ws_lse,
+                                                          T *__restrict__ o,
+                                                          float *__restrict__ lse, int N,
+                                                          int num_splits) {
+    const int64_t hr = blockIdx.x;           // head * N + row
+    const int64_t head = hr / N;
+    const int row = (int)(hr % N);
+    const int lane = threadIdx.x;
+    auto part_lse = [&](int s) { return ws_lse[(head * num_splits + s) * N + row]; };
+
+    float mx = -INFINITY;
+    for (int s = lane; s < num_splits; s += 64) mx = fmaxf(mx, part_lse(s));
+    mx = group_max<64>(mx);
+    T *orow = o + hr * D;
+    if (mx == -INFINITY) {   // no visible key in any segment
+        for (int c = lane; c < D; c += 64) orow[c] = from_f32<T>(0.f);
+        if (lane == 0) lse[hr] = -INFINITY;
+        return;
+    }
+    float z = 0.f;
+    for (int s = lane; s < num_splits; s += 64) z += expf(part_lse(s) - mx);
+    z = group_sum<64>(z);
+    const float total = mx + logf(z);
+    for (int c = lane; c < D; c += 64) {
+        float acc = 0.f;
+        for (int s = 0; s < num_splits; ++s) {
+            const float w = expf(part_lse(s) - total);   // 0 for empty segments
+            acc = fmaf(w, ws_o[((head * num_splits + s) * N + row) * D + c], acc);
+        }
+        orow[c] = from_f32<T>(acc);
+    }
+    if (lane == 0) lse[hr] = total;
+}
+
+template <typename T, int D, int R>
+hipError_t launch_rows(const DecodeArgs &d) {
+    const FwdArgs &a = d.a;
+    const int64_t groups = (a.N + R - 1) / R;
+    dim3 grid((unsigned)d.num_splits, (unsigned)(a.B * a.H), (unsigned)groups);
+    hipLaunchKernelGGL((decode_segment_kernel<T, D, R>), grid, dim3(kThreads), 0, a.stream,
+                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                       static_cast<const T *>(a.v), d.ws_o, d.ws_lse, (int)a.N, (int)a.Nk,
+                       a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)), dim3(64),
+                       0, a.stream, d.ws_o, d.ws_lse, static_cast<T *>(a.o), a.lse, (int)a.N,
+                       d.num_splits);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dim(const DecodeArgs &d) {
+    if (d.a.N == 1) return launch_rows<T, D, 1>(d);
+    return launch_rows<T, D, 4>(d);
+}
+
+template <typename T>
+hipError_t launch_typed(const DecodeArgs &d) {
+    switch (d.a.d) {
+        case 32: return launch_dim<T, 32>(d);
+        case 64: return launch_dim<T, 64>(d);
+        case 128: return launch_dim<T, 128>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_splitkv(const DecodeArgs &d) {
+    switch (d.a.dtype) {
+        case kF32: return launch_typed<float>(d);
+        case kF16: return launch_typed<f16_t>(d);
+        case kBF16: return launch_typed<bf16_t>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,46 @@
+// fa_internal.h -- host-side interface between the C ABI (fa_api.cpp) and
+// the kernel launchers (*.hip).  Arguments reaching a launcher have already
+// been validated: non-null, sizes >= 1, supported (dtype, d, dv), aligned,
+// and every per-head element count below 2^31.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace fa {
+
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct FwdArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;
+    int64_t B, H, N, Nk, d, dv;
+    int causal;
+    float scale;
+    int dtype;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    FwdArgs a;
+    int num_splits;
+    int64_t seg_len;      // keys per segment (multiple of 64)
+    float *ws_o;          // [B, H, num_splits, N, dv]
+    float *ws_lse;        // [B, H, num_splits, N]
+};
+
+// Row-parallel VALU forward: any dtype, d == dv in {32, 64, 128}.
+hipError_t launch_fwd_rowwise(const FwdArgs &a);
+
+// MFMA forward for bf16/fp16 with d == dv in {64, 128} and scale > 0.
+bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale);
+hipError_t launch_fwd_mfma(const FwdArgs &a);
+
+// Split-KV decode: segment kernel then merge kernel, same stream.
+hipError_t launch_decode_splitkv(const DecodeArgs &a);
+
+}  // namespace fa

@@ -1,0 +1,88 @@
+"""Helpers of the GPU parity tests: run the oracle on the same (dtype-rounded)
+inputs the GPU saw and compare element by element.
+
+Tolerances (max absolute error against the FP64 oracle):
+  fp32 inputs:       O <= 2e-5, LSE <= 2e-5
+  bf16/fp16 inputs:  O <= 2e-2, LSE <= 1e-2
+LSE = -inf (a row that sees no key) must match exactly, with O = 0 there.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth_inputs as si
+
+TOL = {"f32": (2e-5, 2e-5), "bf16": (2e-2, 1e-2), "f16": (2e-2, 1e-2)}
+DTYPE_NAME = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def make_inputs(B, H, N, Nk, d, dv, dtype="bf16", seed=0, std=1.0, device="cuda"):
+    """Seeded host draw (numpy), rounded to dtype, placed on the GPU."""
+    q, k, v = si.host_qkv(si.Shape(B, H, N, Nk, d, dv), seed, std)
+    return tuple(si.to_storage(x, dtype, device) for x in (q, k, v))
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what: str, tol=None):
+    """Assert the GPU result matches the oracle; returns (err_o, err_lse).
+    ``tol`` = (tol_o, tol_lse) overrides the per-dtype bar."""
+    tol_o, tol_l = TOL[dtype] if tol is None else tol
+    o = si.as_f64(o_gpu)
+    l = si.as_f64(lse_gpu)
+    assert o.shape == o_ref.shape, (what, o.shape, o_ref.shape)
+    assert l.shape == lse_ref.shape, (what, l.shape, lse_ref.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    ref_empty = np.isneginf(lse_ref)
+    got_empty = np.isneginf(l)
+    assert np.array_equal(ref_empty, got_empty), f"{what}: -inf LSE pattern differs"
+    assert np.all(np.isfinite(l[~got_empty])), f"{what}: non-finite LSE"
+    err_o = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    err_l = float(np.max(np.abs(l[~got_empty] - lse_ref[~ref_empty]))) if (~got_empty).any() else 0.0
+    log(f"  {what}: max|dO|={err_o:.3e} (tol {tol_o:.0e})  max|dLSE|={err_l:.3e} (tol {tol_l:.0e})")
+    assert err_o <= tol_o, f"{what}: O error {err_o:.3e} > {tol_o:.0e}"
+    assert err_l <= tol_l, f"{what}: LSE error {err_l:.3e} > {tol_l:.0e}"
+    return err_o, err_l
+
+
+def oracle_on(q, k, v, causal, scale, heads=None):
+    """Oracle result on the GPU tensors' values; ``heads`` = list of (b, h)."""
+    if heads is None:
+        return oracle.attention(si.as_f64(q), si.as_f64(k), si.as_f64(v), causal=causal, scale=scale)
+    os_, ls_ = [], []
+    for (b, h) in heads:
+        o, l = oracle.attention(si.as_f64(q[b, h]), si.as_f64(k[b, h]), si.as_f64(v[b, h]),
+                                causal=causal, scale=scale)
+        os_.append(o)
+        ls_.append(l)
+    return np.stack(os_), np.stack(ls_)
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def score_scaled_tolerance(q, k, v, scale, dtype: str):
+    """Tolerance for inputs whose scores are far larger than the workloads'.
+
+    A float32 score is a sum of d products; its rounding error grows with
+    the magnitudes summed, about a few units of 2^-24 times
+    s_abs = |scale| * max_ij sum_c |q_ic k_jc|.  A score error e perturbs
+    every weight exp(score) by a relative e, so O moves by up to
+    2 e max|v| (numerator and denominator) and LSE by e.  The bar is the
+    dtype's bar plus that bound with e = 8 * 2^-24 * s_abs."""
+    qa = np.abs(si.as_f64(q))
+    ka = np.abs(si.as_f64(k))
+    va = si.as_f64(v)
+    s_abs = float(np.max(qa @ np.swapaxes(ka, -1, -2))) * abs(scale)
+    e = 8 * 2.0 ** -24 * s_abs
+    base_o, base_l = TOL[dtype]
+    return base_o + 2 * e * float(np.abs(va).max()), base_l + e

@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/fa.h declares, and rejects every invalid call with the documented
+status before touching the GPU.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_flashattention_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# Fake, 16-byte aligned, non-null device addresses.  They are only ever
+# passed in calls that validation must reject before any HIP call; to be
+# safe they are never used when a GPU is visible.
+A = 0x10000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == ["fa_decode_splitkv", "fa_decode_splitkv_workspace_size",
+                                     "fa_fwd", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert fa.status_string(fa.FA_OK) == "FA_OK"
+    assert fa.status_string(fa.FA_ERR_INVALID_ARG) == "FA_ERR_INVALID_ARG"
+    assert fa.status_string(fa.FA_ERR_UNSUPPORTED) == "FA_ERR_UNSUPPORTED"
+    assert fa.status_string(fa.FA_ERR_WORKSPACE) == "FA_ERR_WORKSPACE"
+    assert fa.status_string(fa.FA_ERR_LAUNCH) == "FA_ERR_LAUNCH"
+    assert fa.status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def test_workspace_size_formula():
+    ws = fa.decode_splitkv_workspace_size
+    assert ws(8, 32, 1, 128, 64) == 8 * 32 * 64 * 1 * 129 * 4 == 8454144
+    assert ws(2, 3, 5, 64, 7) == 2 * 3 * 7 * 5 * 65 * 4
+    assert ws(0, 1, 1, 64, 1) == 0
+    assert ws(1, 1, 1, 64, 0) == 0
+    assert ws(1, 1, 1, 0, 4) == 0
+    assert ws(1 << 40, 1 << 20, 1, 128, 64) == 0          # overflow
+
+
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(),
+    reason="fake device pointers are only passed when no GPU is visible")
+
+
+def _fwd(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=4, Nk=4, d=64, dv=64, causal=0, scale=0.125,
+         dtype=2):
+    return fa.library().fa_fwd(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, None)
+
+
+def _dec(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=1, Nk=64, d=64, dv=64, causal=0, scale=0.125,
+         dtype=2, ns=4, ws=A, wsb=1 << 20):
+    return fa.library().fa_decode_splitkv(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale,
+                                          dtype, ns, ws, wsb, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=3), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(q=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(k=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(v=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(N=1 << 40), fa.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 32), fa.FA_ERR_INVALID_ARG),
+    (dict(d=48, dv=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64, dv=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256, dv=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects(kw, expect):
+    assert _fwd(**kw) == expect
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(ns=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ns=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(ns=65537), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=256, H=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 4), fa.FA_ERR_WORKSPACE),
+    (dict(wsb=1 * 1 * 4 * 1 * 65 * 4 - 1), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_rejects(kw, expect):
+    assert _dec(**kw) == expect
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)
+    with pytest.raises(ValueError):
+        fa.decode_splitkv(x, x, x)
