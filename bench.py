@@ -20,6 +20,7 @@ sample of the prefill workload on the host cores, in the same run.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --summarize-pmc DIR   (turn rocprofv3 --pmc CSVs into
                                               the traffic summary under profiles/)
+       python bench.py --summarize-trace DIR (kernel-trace statistics -> profiles/)
 """
 from __future__ import annotations
 
@@ -61,9 +62,17 @@ def decode_bytes(s) -> int:
     return (s.B * s.H * (2 * s.Nk * s.d * e + s.N * s.d * e + s.N * s.dv * e + s.N * 4))
 
 
+COMMON_SRCS = [os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc", n)
+               for n in ("fa_device.h", "fa_internal.h")]
+
+
 def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source together with the headers it includes."""
+    h = hashlib.sha256()
+    for p in [path, *COMMON_SRCS]:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -119,21 +128,27 @@ def summarize_pmc(directory: str) -> None:
     if not rows:
         raise SystemExit(f"no counter_collection.csv under {directory}")
 
-    def per_kernel(counter, pred):
-        vals = [float(r["Counter_Value"]) for r in rows
+    def values(counter, pred):
+        return [float(r["Counter_Value"]) for r in rows
                 if r["Counter_Name"] == counter and pred(r["Kernel_Name"])]
+
+    def per_kernel(counter, pred):
+        vals = values(counter, pred)
         return sum(vals) / len(vals) if vals else None
 
     is_fwd = lambda n: "fwd_mfma_kernel" in n
     is_seg = lambda n: "decode_segment_kernel" in n
     is_merge = lambda n: "decode_merge_kernel" in n
-    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and "fa" not in n[:3]
+    # The 1 GiB calibration copy is a device-to-device memcpy; it is by far the
+    # largest copyBuffer dispatch of the run, so take the largest reading.
+    is_copy = lambda n: "copyBuffer" in n
     out = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        cp = per_kernel(counter, is_copy)
-        if cp is None:
+        cps = values(counter, is_copy)
+        if not cps:
             raise SystemExit(f"no calibration copy kernel found for {counter}")
-        scale = COPY_BYTES / (cp * 1024.0)   # bytes per counted KiB-unit... for the copy
+        cp = max(cps)
+        scale = COPY_BYTES / (cp * 1024.0)   # true bytes per counted byte
         out[counter] = {"copy_kib": cp, "scale": scale,
                         "fwd_kib": per_kernel(counter, is_fwd),
                         "seg_kib": per_kernel(counter, is_seg),
@@ -145,7 +160,12 @@ def summarize_pmc(directory: str) -> None:
     lines = [
         "# HBM traffic per launch from rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE, KiB per",
         "# dispatch, averaged over dispatches), each scaled so that a plain 1 GiB device copy",
-        "# reads and writes exactly 1 GiB.  Made by: python bench.py --summarize-pmc <dir>.",
+        "# reads and writes exactly 1 GiB.  Made by: python bench.py --summarize-pmc <dir>,",
+        "# <dir> holding the CSV output of (run from /tmp, repo at $R):",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/pmc_fetch -o run -- \\",
+        "#       python $R/bench.py --no-cpu-baseline --steps 3 --warmup 1 --calibration-copy",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/pmc_write -o run -- \\",
+        "#       python $R/bench.py --no-cpu-baseline --steps 3 --warmup 1 --calibration-copy",
         f"copy_fetch_kib: {fetch['copy_kib']:.1f}",
         f"copy_write_kib: {write['copy_kib']:.1f}",
         f"fetch_scale: {fetch['scale']:.6f}",
@@ -167,6 +187,36 @@ def summarize_pmc(directory: str) -> None:
     print("\n".join(lines))
 
 
+def summarize_trace(directory: str) -> None:
+    """Write the per-kernel rocprofv3 --kernel-trace --stats summaries of the
+    library's kernels under profiles/, one file per entry point."""
+    import csv
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no kernel_stats.csv under {directory}")
+    rows = list(csv.DictReader(open(paths[0])))
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
+           "python $R/bench.py --no-cpu-baseline   (run from /tmp, repo at $R; 50 timed + 10 "
+           "warm-up steps, each one fa_fwd and one fa_decode_splitkv call)")
+    groups = {
+        f"fwd_mfma_kernel_{PREFILL}.txt": ("fwd_mfma_kernel",),
+        f"decode_splitkv_{DECODE}.txt": ("decode_segment_kernel", "decode_merge_kernel"),
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for fname, keys in groups.items():
+        lines = [f"# rocprofv3 kernel-trace statistics, {fname[:-4]}",
+                 f"# command: {cmd}",
+                 "# kernel | calls | average us | min us | max us | share of traced GPU time %"]
+        for r in rows:
+            if any(k in r["Name"] for k in keys):
+                lines.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                             f"{float(r['Percentage']):.2f}")
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,11 +227,17 @@ def main() -> int:
                     help="prefill heads the CPU oracle is timed on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="add one plain 1 GiB device copy per step (for counter calibration)")
+    ap.add_argument("--only", choices=["prefill", "decode"],
+                    help="profile one entry point alone (the JSON line then omits the other)")
     ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--summarize-trace", metavar="DIR")
     args = ap.parse_args()
 
-    if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
+    if args.summarize_pmc or args.summarize_trace:
+        if args.summarize_pmc:
+            summarize_pmc(args.summarize_pmc)
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -203,6 +259,12 @@ def main() -> int:
     wd = si.WORKLOADS[DECODE]
     sp, sd = wp.shapes[0], wd.shapes[0]
     print(f"# drawing inputs: {wp.description}; {wd.description}", file=sys.stderr, flush=True)
+    run_p = args.only in (None, "prefill")
+    run_d = args.only in (None, "decode")
+    if not run_p:
+        sp = si.Shape(1, 1, 1, 1, sp.d, sp.dv)
+    if not run_d:
+        sd = si.Shape(1, 1, 1, 1, sd.d, sd.dv)
     qp, kp, vp = si.device_qkv(sp, wp.seed, wp.dtype, dev, wp.std)
     qd, kd, vd = si.device_qkv(sd, wd.seed, wd.dtype, dev, wd.std)
     op = torch.empty((sp.B, sp.H, sp.N, sp.dv), dtype=qp.dtype, device=dev)
@@ -222,11 +284,13 @@ def main() -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fwd(qp, kp, vp, causal=True, scale=scale_p, out=op, lse=lp)
+        if run_p:
+            fa.fwd(qp, kp, vp, causal=True, scale=scale_p, out=op, lse=lp)
         if ev is not None:
             ev[1].record(stream)
-        fa.decode_splitkv(qd, kd, vd, causal=False, scale=scale_d, num_splits=wd.num_splits,
-                          workspace=ws, out=od, lse=ld)
+        if run_d:
+            fa.decode_splitkv(qd, kd, vd, causal=False, scale=scale_d, num_splits=wd.num_splits,
+                              workspace=ws, out=od, lse=ld)
         if ev is not None:
             ev[2].record(stream)
         if copy_src is not None:
@@ -305,7 +369,12 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not run_p:
+        result["value"] = None
+        result["roofline"] = None
+    if not run_d:
+        result["decode"] = None
+    if not args.no_cpu_baseline and run_p:
         result["cpu_baseline"] = cpu_baseline(qp, kp, vp, sp, True, min(args.cpu_heads, sp.B * sp.H))
     print(json.dumps(result), flush=True)
     return 0

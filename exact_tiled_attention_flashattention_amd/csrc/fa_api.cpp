@@ -16,6 +16,7 @@ namespace {
 
 constexpr int64_t kMaxI32 = std::numeric_limits<int32_t>::max();
 constexpr int kMaxSplits = 65536;
+constexpr int64_t kMaxHeadBytes = int64_t(1) << 31;
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out) {
     if (a < 0 || b < 0) return false;
@@ -55,6 +56,13 @@ fa_status_t check_common(const void *q, const void *k, const void *v, const void
     if (!mul_ok(heads, t2 > t3 ? t2 : t3, &total) || !mul_ok(heads, t1 > t4 ? t1 : t4, &total))
         return FA_ERR_INVALID_ARG;
     if (!supported_dims(d, dv)) return FA_ERR_UNSUPPORTED;
+    // Kernels address one head's tensors with 32-bit byte offsets and treat
+    // offsets of 3 GiB and more as "outside": each per-head tensor must stay
+    // below 2 GiB.
+    const int64_t esize = dtype == FA_DTYPE_F32 ? 4 : 2;
+    const int64_t per_head_max = t1 > t2 ? (t1 > t3 ? (t1 > t4 ? t1 : t4) : (t3 > t4 ? t3 : t4))
+                                         : (t2 > t3 ? (t2 > t4 ? t2 : t4) : (t3 > t4 ? t3 : t4));
+    if (per_head_max * esize >= kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }
 

@@ -30,7 +30,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kUnroll = 4;   // loads of K (and of V) in flight per lane per step
+constexpr int kUnroll = 8;   // loads of K (and of V) in flight per lane per step
+// A buffer offset beyond any head's K/V extent (at most 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0xC0000000u;
 
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
@@ -83,6 +85,11 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
         for (int i = 0; i < EPL; ++i) acc[r][i] = 0.f;
     }
 
+    // Bounds-checked views of this head's K and V: keys past the segment
+    // are pointed outside them and read as zeros, so the loads need no branch.
+    const auto krs = make_rsrc(kh, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+    const auto vrs = make_rsrc(vh, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+
     // Waves take consecutive steps of KEYS_PER_STEP keys round-robin.
     for (int base = seg_begin + wave * KEYS_PER_STEP; base < seg_end;
          base += kWaves * KEYS_PER_STEP) {
@@ -90,13 +97,11 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int key = base + u * KPL + slot;
-            if (key < seg_end) {
-                kraw[u] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)key * D + t * EPL);
-                vraw[u] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)key * D + t * EPL);
-            } else {
-                kraw[u] = u32x4{0u, 0u, 0u, 0u};
-                vraw[u] = u32x4{0u, 0u, 0u, 0u};
-            }
+            const uint32_t off = key < seg_end
+                                     ? ((uint32_t)key * D + t * EPL) * (uint32_t)sizeof(T)
+                                     : kOutOfRange;
+            kraw[u] = buffer_load16(krs, off);
+            vraw[u] = buffer_load16(vrs, off);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -168,41 +173,77 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     }
 }
 
-// One wave per (head, row): merge num_splits partial states.
+// One workgroup of 4 waves per (head, row): merge num_splits partial states.
+// Every lane first takes some segments' lse_s to find M = max lse_s and
+// Z = sum exp(lse_s - M) (wave reductions, then across the 4 waves through
+// LDS); then the weights w_s = exp(lse_s - lse) of a chunk of 64 segments
+// are computed once, one per lane, and staged in LDS, and each wave
+// accumulates w_s * o_s over its share of the chunk's segments with the
+// row's columns spread over its lanes; the 4 partial sums meet in LDS.
+constexpr int kMergeWaves = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restrict__ ws_o,
-                                                          const float *__restrict__ ws_lse,
-                                                          T *__restrict__ o,
-                                                          float *__restrict__ lse, int N,
-                                                          int num_splits) {
-    const int64_t hr = blockIdx.x;           // head * N + row
+__global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(
+    const float *__restrict__ ws_o, const float *__restrict__ ws_lse, T *__restrict__ o,
+    float *__restrict__ lse, int N, int num_splits) {
+    constexpr int CPL = D >= 64 ? D / 64 : 1;      // columns per lane
+    const int64_t hr = blockIdx.x;                  // head * N + row
     const int64_t head = hr / N;
     const int row = (int)(hr % N);
-    const int lane = threadIdx.x;
-    auto part_lse = [&](int s) { return ws_lse[(head * num_splits + s) * N + row]; };
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t base = head * (int64_t)num_splits * N + row;   // segment s at base + s*N
+    __shared__ float red[2][kMergeWaves];
+    __shared__ float wts[64];
+    __shared__ float part[kMergeWaves][D];
 
     float mx = -INFINITY;
-    for (int s = lane; s < num_splits; s += 64) mx = fmaxf(mx, part_lse(s));
+    for (int s = tid; s < num_splits; s += kMergeWaves * 64) mx = fmaxf(mx, ws_lse[base + (int64_t)s * N]);
     mx = group_max<64>(mx);
+    if (lane == 0) red[0][wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     T *orow = o + hr * D;
     if (mx == -INFINITY) {   // no visible key in any segment
-        for (int c = lane; c < D; c += 64) orow[c] = from_f32<T>(0.f);
-        if (lane == 0) lse[hr] = -INFINITY;
+        for (int c = tid; c < D; c += kMergeWaves * 64) orow[c] = from_f32<T>(0.f);
+        if (tid == 0) lse[hr] = -INFINITY;
         return;
     }
     float z = 0.f;
-    for (int s = lane; s < num_splits; s += 64) z += expf(part_lse(s) - mx);
+    for (int s = tid; s < num_splits; s += kMergeWaves * 64) z += expf(ws_lse[base + (int64_t)s * N] - mx);
     z = group_sum<64>(z);
+    if (lane == 0) red[1][wave] = z;
+    __syncthreads();
+    z = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
     const float total = mx + logf(z);
-    for (int c = lane; c < D; c += 64) {
-        float acc = 0.f;
-        for (int s = 0; s < num_splits; ++s) {
-            const float w = expf(part_lse(s) - total);   // 0 for empty segments
-            acc = fmaf(w, ws_o[((head * num_splits + s) * N + row) * D + c], acc);
+
+    float acc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+    const int col0 = lane * CPL;
+    for (int s0 = 0; s0 < num_splits; s0 += 64) {
+        const int cnt = min(64, num_splits - s0);
+        __syncthreads();   // previous chunk's weights consumed
+        if (tid < cnt) wts[tid] = expf(ws_lse[base + (int64_t)(s0 + tid) * N] - total);   // 0 if empty
+        __syncthreads();
+        if (col0 < D) {
+#pragma unroll 4
+            for (int i = wave; i < cnt; i += kMergeWaves) {
+                const float w = wts[i];
+                const float *src = ws_o + (base + (int64_t)(s0 + i) * N) * D + col0;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w, src[c], acc[c]);
+            }
         }
-        orow[c] = from_f32<T>(acc);
     }
-    if (lane == 0) lse[hr] = total;
+    if (col0 < D) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) part[wave][col0 + c] = acc[c];
+    }
+    __syncthreads();
+    for (int c = tid; c < D; c += kMergeWaves * 64)
+        orow[c] = from_f32<T>((part[0][c] + part[1][c]) + (part[2][c] + part[3][c]));
+    if (tid == 0) lse[hr] = total;
 }
 
 template <typename T, int D, int R>
@@ -216,7 +257,8 @@ hipError_t launch_rows(const DecodeArgs &d) {
                        a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)), dim3(64),
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)),
+                       dim3(kMergeWaves * 64),
                        0, a.stream, d.ws_o, d.ws_lse, static_cast<T *>(a.o), a.lse, (int)a.N,
                        d.num_splits);
     return hipGetLastError();

@@ -74,8 +74,41 @@ __device__ __forceinline__ float swap32(float x) {
 }
 
 // 16-byte vector of raw bits.
-struct alignas(16) u32x4 {
-    uint32_t x, y, z, w;
-};
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- buffer loads --------------------------------------------------------
+// A raw buffer resource over `bytes` bytes at `base`: loads at byte offsets
+// past the end return zeros instead of touching memory, so ragged tiles
+// need no branch around the load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+}
+
+// The same raw buffer resource as four scalar words (for inline assembly).
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// Memory -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane i's bytes at buffer offset `voff` land at LDS address lds_addr + 16 i.
+// Issued as inline assembly so that the compiler does not track it: the
+// caller waits for it (s_waitcnt vmcnt) and publishes it (s_barrier) itself.
+// Out-of-range offsets write zeros.  `lds_addr` must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
 
 }  // namespace fa

@@ -39,6 +39,8 @@
 //    one XCD (the hardware deals workgroup ids round-robin over the 8 XCDs),
 //    keeping a head's K/V hot in that XCD's L2; under the causal mask the
 //    longest query blocks of each head are issued first.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -48,6 +50,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
@@ -56,6 +59,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBR = 128;            // query rows per workgroup
 constexpr int kQW = kBR / kWaves;   // query rows per wave (two 16-row blocks)
 constexpr int kBC = 64;             // keys per tile
+// A buffer offset beyond any head's K/V extent (at most 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0xC0000000u;
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -72,17 +77,46 @@ template <> struct Mfma<f16_t> {
 };
 
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+// The maximum propagates NaN and needs no operand canonicalisation.
 __device__ __forceinline__ float rows_max(float x) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-    x = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+    x = __builtin_elementwise_maximum(__int_as_float(a[0]), __int_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+    return __builtin_elementwise_maximum(__int_as_float(b[0]), __int_as_float(b[1]));
 }
 __device__ __forceinline__ float rows_sum(float x) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
     x = __int_as_float(a[0]) + __int_as_float(a[1]);
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
     return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+// acc + sum of the 8 probabilities of a B operand, as rounded for the MFMA
+// (v_dot2 against (1, 1) pairs), so numerator and denominator see the same P.
+__device__ __forceinline__ float row_sum_pairs(bf16x8 t, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 6, 7), one, acc, false);
+    return acc;
+}
+__device__ __forceinline__ float row_sum_pairs(f16x8 t, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 6, 7), one, acc, false);
+    return acc;
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their "no wait" maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // LDS swizzles.  K: 16-byte chunk c of key row r is stored at chunk
@@ -98,7 +132,7 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     T *__restrict__ o, float *__restrict__ lse, int N, int Nk, float c,
     int q_blocks, int num_wg) {
@@ -110,10 +144,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
     constexpr int ROWB = D * 2;                 // bytes per key row
     constexpr int TILE = kBC * ROWB;            // bytes per K (or V) tile
     constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-    constexpr int CPT = TILE / 16 / kThreads;   // chunks per thread per tile
-    static_assert(CPT * 16 * kThreads == TILE, "tile split");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TILE];   // [buf][K,V]
+    constexpr int NBUF = (D == 64) ? 3 : 2;     // LDS stages (tiles in flight)
+    constexpr int LPT = TILE / 1024 / kWaves;  // 1 KiB wave loads per wave per K (or V) tile
+    static_assert(LPT * 1024 * kWaves == TILE, "tile split");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF][2][TILE];   // [stage][K,V]
 
     // ---- workgroup -> (head, query block) ---------------------------------
     const int w = blockIdx.x;
@@ -125,16 +160,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
     if (CAUSAL) qblk = q_blocks - 1 - qblk;
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wave
     const int lane = tid % 64;
     const int g = lane / 16;    // lane row (0..3)
     const int li = lane % 16;   // lane column
     const int q0 = qblk * kBR;
     const int qw0 = q0 + wave * kQW;
 
-    const T *qh = q + (int64_t)head * N * D;
-    const T *kh = k + (int64_t)head * Nk * D;
-    const T *vh = v + (int64_t)head * Nk * D;
+    // Bounds-checked views of this head's Q, K, V (reads past the end give 0).
+    const auto qrs = make_rsrc(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
 
     // ---- Q^T operands: lane holds Q[qw0 + qb*16 + li][ks*32 + 8g .. +7] ---
     vec8 qop[2][KS];
@@ -143,9 +177,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
         const int row = qw0 + qb * 16 + li;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 raw = {0u, 0u, 0u, 0u};
-            if (row < N) raw = *reinterpret_cast<const u32x4 *>(qh + (int64_t)row * D + ks * 32 + 8 * g);
-            qop[qb][ks] = __builtin_bit_cast(vec8, raw);
+            const uint32_t off = ((uint32_t)row * D + ks * 32 + 8 * g) * 2u;
+            qop[qb][ks] = __builtin_bit_cast(vec8, buffer_load16(qrs, off));
         }
     }
 
@@ -158,31 +191,42 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
     }
     const int ntiles = key_end > 0 ? (key_end + kBC - 1) / kBC : 0;
 
-    u32x4 kreg[CPT], vreg[CPT];
-    auto fetch = [&](int j) {
+    // K/V tiles go straight from memory to LDS (buffer_load ... lds): each
+    // wave load writes 1 KiB of LDS, lane i's 16 bytes at offset 16 i, so the
+    // swizzled layout is produced by choosing which global 16-byte piece each
+    // lane fetches.  A tile index past the last one points the load outside
+    // the buffers, which writes zeros and touches no memory.
+    typedef __attribute__((address_space(3))) void lds_void;
+    uint32_t koff[LPT], voff[LPT];   // per-lane global byte offsets within a tile
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int chunk = tid + kThreads * i;
-            const int row = chunk / CPR, col = chunk % CPR;
-            const int key = j * kBC + row;
-            if (key < Nk) {
-                kreg[i] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)key * D + col * 8);
-                vreg[i] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)key * D + col * 8);
-            } else {
-                kreg[i] = u32x4{0u, 0u, 0u, 0u};
-                vreg[i] = u32x4{0u, 0u, 0u, 0u};
-            }
+    for (int t = 0; t < LPT; ++t) {
+        const int slot = (t * kWaves + wave) * 64 + lane;   // 16-byte slot in the tile
+        const int row = slot / CPR, pc = slot % CPR;
+        koff[t] = ((uint32_t)row * D + (pc ^ kswz<D>(row)) * 8) * 2u;
+        voff[t] = ((uint32_t)row * D + (((2 * pc) ^ vswz<D>(row)) / 2) * 8) * 2u;
+    }
+    const u32x4 kw = rsrc_words(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const u32x4 vw = rsrc_words(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_void *)&smem[0][0][0];
+    auto issue = [&](int j) {
+        const int stage = j % NBUF;
+        const uint32_t tile_off = j < ntiles ? (uint32_t)j * kBC * D * 2u : kOutOfRange;
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const uint32_t dst = lds0 + stage * 2 * TILE + (t * kWaves + wave) * 1024;
+            lds_dma16(kw, __builtin_amdgcn_readfirstlane(dst), tile_off + koff[t]);
+            lds_dma16(vw, __builtin_amdgcn_readfirstlane(dst + TILE), tile_off + voff[t]);
         }
     };
-    auto stash = [&](int buf) {
+
+    // Per-lane mask bound: key j0 + kb*16 + 4g + r is visible to query qi iff
+    // kb*16 + r <= lim[qb] - j0, with lim = (last key qi sees) - 4g.
+    int lim[2];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int chunk = tid + kThreads * i;
-            const int row = chunk / CPR, col = chunk % CPR;
-            *reinterpret_cast<u32x4 *>(&smem[buf][0][row * ROWB + ((col ^ kswz<D>(row)) * 16)]) = kreg[i];
-            *reinterpret_cast<u32x4 *>(&smem[buf][1][row * ROWB + (((2 * col) ^ vswz<D>(row)) * 8)]) = vreg[i];
-        }
-    };
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + qb * 16 + li;
+        lim[qb] = (CAUSAL ? min(Nk - 1, Nk - N + qi) : Nk - 1) - 4 * g;
+    }
 
     float m[2] = {-INFINITY, -INFINITY};   // running max of scaled scores (base 2)
     float l[2] = {0.f, 0.f};               // per-lane partial row sums
@@ -192,18 +236,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (ntiles > 0) {
-        fetch(0);
-        stash(0);
-    }
-    __syncthreads();
+    // One tile of the loop.  Masked tiles straddle the diagonal or the end of
+    // the keys.
+    auto tile = [&](const int buf, const int j0, const bool masked) {
 
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        const int j0 = j * kBC;
-        if (j + 1 < ntiles) fetch(j + 1);
-
-        // ---- S^T = K Q^T for this tile ------------------------------------
+        // ---- S^T = K Q^T ----------------------------------------------------
         const unsigned char *ks_base = smem[buf][0];
         f32x4 s[KB][2];
 #pragma unroll
@@ -219,58 +256,62 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
                 s[kb][1] = Mfma<T>::run(a, qop[1][ks], s[kb][1]);
             }
         }
+        if (masked) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int t = lim[qb] - j0;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (kb * 16 + r > t) s[kb][qb][r] = -INFINITY;
+            }
+        }
 
-        // ---- mask tiles that straddle the diagonal or the end of the keys --
-        if (j0 + kBC > full_end) {
+        // ---- online softmax with lazy rescaling ------------------------------
+        // The running max m only moves when a row's tile max exceeds it by
+        // more than 8 (base 2); otherwise the stale m is kept, so the
+        // probabilities stay <= 2^8 and the accumulator needs no rescale.
+        // The result is unchanged: O and l share the same m.
+        float mt[2];
+        bool need[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float x = s[0][qb][0];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    const int qi = qw0 + qb * 16 + li;
-                    const int limit = CAUSAL ? min(Nk - 1, Nk - N + qi) : Nk - 1;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = j0 + kb * 16 + 4 * g + r;
-                        if (key > limit) s[kb][qb][r] = -INFINITY;
-                    }
-                }
+                for (int r = 0; r < 4; ++r) x = __builtin_elementwise_maximum(x, s[kb][qb][r]);
+            mt[qb] = rows_max(x) * c;
+            need[qb] = mt[qb] > m[qb] + 8.f;
         }
-
-        // ---- online softmax (scaled base-2 domain) --------------------------
+        if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float m_new = need[qb] ? mt[qb] : m[qb];
+                const float alpha = fast_exp2(m[qb] - m_new);   // 0 when m = -inf < m_new
+                const float a = need[qb] ? alpha : 1.f;
+                l[qb] *= a;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db][qb] *= a;
+                m[qb] = m_new;
+            }
+        }
         vec8 pb[PC][2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            float mx = s[0][qb][0];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-            mx = rows_max(mx);
-            const float m_new = fmaxf(m[qb], mx * c);
-            const float alpha = (m[qb] == -INFINITY) ? 0.f : fast_exp2(m[qb] - m_new);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            float p[KB][4];
-            float lsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    p[kb][r] = fast_exp2(fmaf(s[kb][qb][r], c, -m_use));
-                    lsum += p[kb][r];
-                }
-            l[qb] = fmaf(l[qb], alpha, lsum);
-            m[qb] = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+            const float m_use = (m[qb] == -INFINITY) ? 0.f : m[qb];
 #pragma unroll
             for (int pc = 0; pc < PC; ++pc) {
-                vec8 t;
+                f32x8 pf;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    t[r] = static_cast<T>(p[2 * pc][r]);
-                    t[4 + r] = static_cast<T>(p[2 * pc + 1][r]);
-                }
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pf[4 * h + r] = fast_exp2(fmaf(s[2 * pc + h][qb][r], c, -m_use));
+                const vec8 t = __builtin_convertvector(pf, vec8);
                 pb[pc][qb] = t;
+                l[qb] = row_sum_pairs(t, l[qb]);
             }
         }
 
@@ -278,25 +319,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(
         const unsigned char *vs_base = smem[buf][1];
 #pragma unroll
         for (int pc = 0; pc < PC; ++pc) {
+            {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int r_lo = pc * 32 + 4 * g + li / 4;
-                const int r_hi = r_lo + 16;
-                const int u = 4 * db + (li % 4);
-                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                lds_i16x4 *p_lo = (lds_i16x4 *)(vs_base + r_lo * ROWB + ((u ^ vswz<D>(r_lo)) * 8));
-                lds_i16x4 *p_hi = (lds_i16x4 *)(vs_base + r_hi * ROWB + ((u ^ vswz<D>(r_hi)) * 8));
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p_lo);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p_hi);
-                const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                const vec8 a = __builtin_bit_cast(vec8, both);
-                oacc[db][0] = Mfma<T>::run(a, pb[pc][0], oacc[db][0]);
-                oacc[db][1] = Mfma<T>::run(a, pb[pc][1], oacc[db][1]);
+                for (int db = 0; db < DB; ++db) {
+                    const int r_lo = pc * 32 + 4 * g + li / 4;
+                    const int r_hi = r_lo + 16;
+                    const int u = 4 * db + (li % 4);
+                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                    lds_i16x4 *p_lo = (lds_i16x4 *)(vs_base + r_lo * ROWB + ((u ^ vswz<D>(r_lo)) * 8));
+                    lds_i16x4 *p_hi = (lds_i16x4 *)(vs_base + r_hi * ROWB + ((u ^ vswz<D>(r_hi)) * 8));
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p_lo);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p_hi);
+                    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const vec8 a = __builtin_bit_cast(vec8, both);
+                    oacc[db][0] = Mfma<T>::run(a, pb[pc][0], oacc[db][0]);
+                    oacc[db][1] = Mfma<T>::run(a, pb[pc][1], oacc[db][1]);
+                }
             }
         }
+    };
 
-        if (j + 1 < ntiles) stash(buf ^ 1);
-        __syncthreads();
+    // Tile j is waited for (this wave's loads via vmcnt, everyone's via the
+    // barrier, which also frees the stage tile j-1 used), then tile
+    // j+NBUF-1 is issued into that freed stage, then tile j is consumed.
+    // The explicit wait leaves the loads of the NBUF-2 later tiles in flight.
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p) issue(p);
+    // Re-define the Q operands here so that the loop carries no dependence on
+    // their loads (the loop would otherwise wait for every outstanding load).
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[qb][ks]));
+    for (int j = 0; j < ntiles; ++j) {
+        wait_vmcnt<2 * LPT * (NBUF - 2)>();
+        __builtin_amdgcn_s_barrier();
+        issue(j + NBUF - 1);
+        const int j0 = j * kBC;
+        tile(j % NBUF, j0, j0 + kBC > full_end);
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------

@@ -81,6 +81,8 @@ typedef enum {
  *   B, H     batch and head counts (>= 1).
  *   N, Nk    query rows and keys per head (>= 1).
  *   d, dv    head dims of q/k and of v/o.  Supported: d == dv in {32, 64, 128}.
+ *            Each per-head slice (N*d, Nk*d, Nk*dv, N*dv elements) must be
+ *            smaller than 2 GiB, else FA_ERR_UNSUPPORTED.
  *   causal   0: no mask; non-zero: bottom-right causal mask (see above).
  *   scale    multiplies Q K^T before the softmax; any finite value (0 gives
  *            uniform weights over the visible keys).  The usual value 1/sqrt(d)

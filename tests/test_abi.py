@@ -97,6 +97,8 @@ def _dec(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=1, Nk=64, d=64, dv=64, causal=0,
     (dict(d=48, dv=48), fa.FA_ERR_UNSUPPORTED),
     (dict(d=64, dv=128), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256, dv=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=1 << 22, d=128, dv=128, dtype=0), fa.FA_ERR_UNSUPPORTED),   # 2 GiB per head
+    (dict(N=1 << 23, d=128, dv=128, dtype=2), fa.FA_ERR_UNSUPPORTED),    # 2 GiB per head
 ])
 def test_fwd_rejects(kw, expect):
     assert _fwd(**kw) == expect
