@@ -3,7 +3,7 @@
 // bf16/fp16 inputs, d == dv in {64, 128}, scale > 0; fp32 accumulation.
 //
 // Method: the FlashAttention-2 loop order of CS349E Lecture 11
-// "flash_lab.py", section 3 (flash_fwd, order "fa2"): one block of 128
+// "flash_lab.py", section 3 (flash_fwd, order "fa2"): one block of 256
 // query rows per workgroup; the head's K/V tiles (64 keys) stream through
 // LDS; per tile the scores of the block are formed on chip, the running row
 // maximum and row sum are updated with section 1's online-softmax rescaling,
@@ -13,7 +13,7 @@
 // block's last visible key are never loaded and only tiles that straddle
 // the diagonal or the end of the keys pay for masking.
 //
-// gfx950 mapping (4 waves, 32 query rows per wave):
+// gfx950 mapping (8 waves in two groups of four, 32 query rows per wave):
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_{bf16,f16}: K is the A operand (read from LDS with
 //    ds_read_b128), Q^T the B operand (loaded once into registers).  The
@@ -27,18 +27,18 @@
 //    index is read as the key order {4g..4g+3, 16+4g..16+4g+3}.  V^T (the
 //    A operand) is read from the row-major V tile with ds_read_b64_tr_b16,
 //    which hands each lane four consecutive keys of one value column, in
-//    that same key order.
-//  * LDS tiles are XOR-swizzled per row (16-byte chunks for K, 32-byte
-//    groups for V) so that the A-operand reads of K and the transposing
-//    reads of V hit distinct banks.  Two buffers: while tile j is consumed,
-//    tile j+1 is fetched with 16-byte global loads into registers and
-//    written to the other buffer afterwards; one barrier per tile.
-//  * The row sum is kept per lane (over that lane's keys) and reduced
-//    across the 4 lane groups only in the epilogue.
-//  * Workgroups are numbered so that consecutive work of one head lands on
-//    one XCD (the hardware deals workgroup ids round-robin over the 8 XCDs),
-//    keeping a head's K/V hot in that XCD's L2; under the causal mask the
-//    longest query blocks of each head are issued first.
+//    that same key order.  An all-ones A operand yields the row sums.
+//  * The two wave groups alternate between matrix-core work and softmax
+//    work in intervals separated by barriers (ping-pong), so the two waves
+//    of a SIMD (w and w + 4) overlap the matrix core and the vector ALU.
+//  * K/V tiles are copied from memory straight into LDS (three stages each)
+//    and XOR-swizzled per row (16-byte chunks for K, 32-byte groups for V)
+//    so that the A-operand reads of K and the transposing reads of V are
+//    free of bank conflicts; the loop is unrolled over the three stages so
+//    that every LDS address is a register plus an immediate.
+//  * The kernel is persistent: each workgroup walks units of two query
+//    blocks of one head whose causal costs add up to a constant, numbered
+//    so that workgroups of one XCD share heads (K/V reuse in that L2).
 #include <type_traits>
 
 #include "fa_device.h"
@@ -54,14 +54,13 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 4;
+// Eight waves in two groups of four; waves w and w + 4 share a SIMD.  Group
+// gamma owns query rows [128 gamma, 128 gamma + 128) of the block, 32 per wave.
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBR = 128;            // query rows per workgroup
-constexpr int kQW = kBR / kWaves;   // query rows per wave (two 16-row blocks)
+constexpr int kBR = 256;            // query rows per workgroup
+constexpr int kQW = 32;             // query rows per wave (two 16-row blocks)
 constexpr int kBC = 64;             // keys per tile
-// A buffer offset beyond any head's K/V extent (at most 2^31 bytes).
-constexpr uint32_t kOutOfRange = 0xC0000000u;
-
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
     typedef bf16x8 vec;
@@ -84,34 +83,6 @@ __device__ __forceinline__ float rows_max(float x) {
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
     return __builtin_elementwise_maximum(__int_as_float(b[0]), __int_as_float(b[1]));
 }
-__device__ __forceinline__ float rows_sum(float x) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
-    x = __int_as_float(a[0]) + __int_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return __int_as_float(b[0]) + __int_as_float(b[1]);
-}
-
-// acc + sum of the 8 probabilities of a B operand, as rounded for the MFMA
-// (v_dot2 against (1, 1) pairs), so numerator and denominator see the same P.
-__device__ __forceinline__ float row_sum_pairs(bf16x8 t, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 4, 5), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t, t, 6, 7), one, acc, false);
-    return acc;
-}
-__device__ __forceinline__ float row_sum_pairs(f16x8 t, float acc) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 4, 5), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(t, t, 6, 7), one, acc, false);
-    return acc;
-}
-
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their "no wait" maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -123,7 +94,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // c ^ kswz(r).  V: 8-byte quad u of row r is stored at quad u ^ vswz(r)
 // (a multiple of 4, so 16-byte chunks stay whole).
 template <int D> __device__ __forceinline__ int kswz(int r) {
-    if constexpr (D == 64) return (r & 7) ^ ((r >> 3) & 1);
+    if constexpr (D == 64)
+        return ((r >> 2) & 1) | ((__builtin_popcount(r & 15) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
     else return r & 15;
 }
 template <int D> __device__ __forceinline__ int vswz(int r) {
@@ -132,10 +104,10 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     T *__restrict__ o, float *__restrict__ lse, int N, int Nk, float c,
-    int q_blocks, int num_wg) {
+    int q_blocks, int n_items) {
     typedef typename Mfma<T>::vec vec8;
     constexpr int KS = D / 32;                  // contraction steps of S (d)
     constexpr int DB = D / 16;                  // 16-wide value blocks of O
@@ -144,28 +116,66 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
     constexpr int ROWB = D * 2;                 // bytes per key row
     constexpr int TILE = kBC * ROWB;            // bytes per K (or V) tile
     constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-
-    constexpr int NBUF = (D == 64) ? 3 : 2;     // LDS stages (tiles in flight)
-    constexpr int LPT = TILE / 1024 / kWaves;  // 1 KiB wave loads per wave per K (or V) tile
+    constexpr int NK = 3, NV = 3;               // LDS stages of K and of V
+    constexpr int LPT = TILE / 1024 / kWaves;   // 1 KiB wave loads per wave per K (or V) tile
     static_assert(LPT * 1024 * kWaves == TILE, "tile split");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF][2][TILE];   // [stage][K,V]
-
-    // ---- workgroup -> (head, query block) ---------------------------------
-    const int w = blockIdx.x;
-    const int per = num_wg / 8, rem = num_wg % 8;
-    const int xcd = w % 8, idx = w / 8;
-    const int L = xcd * per + min(xcd, rem) + idx;
-    const int head = L / q_blocks;
-    int qblk = L % q_blocks;
-    if (CAUSAL) qblk = q_blocks - 1 - qblk;
+    __shared__ __attribute__((aligned(16))) unsigned char kbuf[NK][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NV][TILE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wave
+    const int grp = wave / 4;   // 0: group A, 1: group B
     const int lane = tid % 64;
     const int g = lane / 16;    // lane row (0..3)
     const int li = lane % 16;   // lane column
+
+    // Per-lane LDS byte offsets of the MFMA operand reads within a tile; the
+    // rest of each address (stage, key block) is a compile-time constant.
+    //  K (A operand of S^T): key row kb*16 + li, 16-byte chunk ks*4 + g.
+    //  V (ds_read_b64_tr_b16): key row 4g + li/4 (+16, +32 pc), quad 4 db + li%4.
+    uint32_t kofs[D / 32], vofs[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kofs[ks] = li * (2 * D) + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const int r0 = 4 * g + li / 4;
+        vofs[db] = r0 * (2 * D) + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+    }
+    vec8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = static_cast<T>(1.0f);
+
+    // ---- persistent loop over work units ---------------------------------------
+    // A unit is a pair of query blocks of one head, p and QB-1-p (the middle
+    // block alone when QB is odd): under the causal mask their key counts add
+    // up to the same total for every p, so units cost the same and a plain
+    // round-robin of units over the G resident workgroups is balanced.  The
+    // two blocks of a unit reuse the head's K/V from L2.  When G and the head
+    // count are multiples of 8, units are numbered so that the workgroups of
+    // one XCD (ids congruent mod 8) work on the same heads at the same time.
+    const int G = gridDim.x;
+    const int n_heads = n_items / q_blocks;
+    const int U = (q_blocks + 1) / 2;   // units per head
+    const int n_units = n_heads * U;
+    const bool xcd_map = (G % 8 == 0) && (n_heads % 8 == 0);
+    for (int u = blockIdx.x; u < n_units; u += G)
+    for (int half = 0; half < 2; ++half) {
+    int head, pair;
+    if (xcd_map) {
+        const int local = u / 8;
+        head = (local / U) * 8 + u % 8;
+        pair = local % U;
+    } else {
+        head = u / U;
+        pair = u % U;
+    }
+    const int qblk = half == 0 ? pair : q_blocks - 1 - pair;
+    if (half == 1 && qblk == pair) break;   // odd middle block: single item
+    // The previous item's LDS reads and copies are finished everywhere.
+    __syncthreads();
+
     const int q0 = qblk * kBR;
-    const int qw0 = q0 + wave * kQW;
+    const int qw0 = q0 + grp * (kBR / 2) + (wave % 4) * kQW;
 
     // Bounds-checked views of this head's Q, K, V (reads past the end give 0).
     const auto qrs = make_rsrc(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
@@ -182,20 +192,25 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
         }
     }
 
-    // ---- key range of this block ------------------------------------------
-    int key_end = Nk;
-    int full_end = Nk;   // keys below this are visible to every query of the block
+    // ---- key ranges ---------------------------------------------------------
+    // The block streams the tiles up to its last visible key; a wave computes
+    // only the tiles its own rows can see and masks those that reach past
+    // the keys every one of its rows sees (none if all its rows are past N).
+    int key_end = Nk;        // block
+    int wave_end = Nk;       // this wave: keys below are visible to some row
+    int full_end = Nk;       // this wave: keys below are visible to every row
     if (CAUSAL) {
         key_end = min(Nk, Nk - N + min(q0 + kBR, N));
-        full_end = min(Nk, Nk - N + q0 + 1);
+        wave_end = min(Nk, Nk - N + min(qw0 + kQW, N));
+        full_end = min(Nk, Nk - N + qw0 + 1);
     }
     const int ntiles = key_end > 0 ? (key_end + kBC - 1) / kBC : 0;
+    const int wtiles = (wave_end > 0 && qw0 < N) ? (wave_end + kBC - 1) / kBC : 0;
 
     // K/V tiles go straight from memory to LDS (buffer_load ... lds): each
     // wave load writes 1 KiB of LDS, lane i's 16 bytes at offset 16 i, so the
     // swizzled layout is produced by choosing which global 16-byte piece each
-    // lane fetches.  A tile index past the last one points the load outside
-    // the buffers, which writes zeros and touches no memory.
+    // lane fetches.  Rows past Nk read as zeros (buffer bounds check).
     typedef __attribute__((address_space(3))) void lds_void;
     uint32_t koff[LPT], voff[LPT];   // per-lane global byte offsets within a tile
 #pragma unroll
@@ -207,15 +222,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
     }
     const u32x4 kw = rsrc_words(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
     const u32x4 vw = rsrc_words(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
-    const uint32_t lds0 = (uint32_t)(size_t)(lds_void *)&smem[0][0][0];
-    auto issue = [&](int j) {
-        const int stage = j % NBUF;
-        const uint32_t tile_off = j < ntiles ? (uint32_t)j * kBC * D * 2u : kOutOfRange;
+    const uint32_t klds = (uint32_t)(size_t)(lds_void *)&kbuf[0][0];
+    const uint32_t vlds = (uint32_t)(size_t)(lds_void *)&vbuf[0][0];
+    auto issue_k = [&](int j) {
+        if (j >= ntiles) return;
+        const uint32_t tile_off = (uint32_t)j * kBC * D * 2u;
 #pragma unroll
         for (int t = 0; t < LPT; ++t) {
-            const uint32_t dst = lds0 + stage * 2 * TILE + (t * kWaves + wave) * 1024;
+            const uint32_t dst = klds + (j % NK) * TILE + (t * kWaves + wave) * 1024;
             lds_dma16(kw, __builtin_amdgcn_readfirstlane(dst), tile_off + koff[t]);
-            lds_dma16(vw, __builtin_amdgcn_readfirstlane(dst + TILE), tile_off + voff[t]);
+        }
+    };
+    auto issue_v = [&](int j) {
+        if (j >= ntiles) return;
+        const uint32_t tile_off = (uint32_t)j * kBC * D * 2u;
+#pragma unroll
+        for (int t = 0; t < LPT; ++t) {
+            const uint32_t dst = vlds + (j % NV) * TILE + (t * kWaves + wave) * 1024;
+            lds_dma16(vw, __builtin_amdgcn_readfirstlane(dst), tile_off + voff[t]);
         }
     };
 
@@ -229,34 +253,81 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
     }
 
     float m[2] = {-INFINITY, -INFINITY};   // running max of scaled scores (base 2)
-    float l[2] = {0.f, 0.f};               // per-lane partial row sums
+    f32x4 lacc[2];                         // row sums (every register holds the sum)
     f32x4 oacc[DB][2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+        lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4 s[KB][2];      // scores of the current tile
+    vec8 pb[PC][2];      // probabilities of the previous tile (B operands)
+    // Empty asm that claims to modify its operands: the values must be
+    // computed before this point and are not moved (sunk) past it, which
+    // keeps each phase's work inside its interval.
+    auto pin_scores = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(s[kb][0]), "+v"(s[kb][1]));
+    };
+    auto pin_acc = [&]() {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(oacc[db][0]), "+v"(oacc[db][1]));
+        asm volatile("" : "+v"(lacc[0]), "+v"(lacc[1]));
+    };
+    auto pin_probs = [&]() {
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) asm volatile("" : "+v"(pb[pc][0]), "+v"(pb[pc][1]));
+        asm volatile("" : "+v"(m[0]), "+v"(m[1]));
+    };
 
-    // One tile of the loop.  Masked tiles straddle the diagonal or the end of
-    // the keys.
-    auto tile = [&](const int buf, const int j0, const bool masked) {
-
-        // ---- S^T = K Q^T ----------------------------------------------------
-        const unsigned char *ks_base = smem[buf][0];
-        f32x4 s[KB][2];
+    // ---- S^T = K Q^T for the K tile in stage SK ---------------------------------
+    auto scores = [&](auto SK) {
+        const unsigned char *base = kbuf[0] + decltype(SK)::value * TILE;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             s[kb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
             s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int row = kb * 16 + li;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int chunk = (ks * 4 + g) ^ kswz<D>(row);
-                const vec8 a = *reinterpret_cast<const vec8 *>(ks_base + row * ROWB + chunk * 16);
+                const vec8 a = *reinterpret_cast<const vec8 *>(base + kb * 16 * ROWB + kofs[ks]);
                 s[kb][0] = Mfma<T>::run(a, qop[0][ks], s[kb][0]);
                 s[kb][1] = Mfma<T>::run(a, qop[1][ks], s[kb][1]);
             }
-        }
-        if (masked) {
+        }        pin_scores();
+    };
+
+    // ---- O^T += V^T P^T for the V tile in stage SV -----------------------------
+    // The row sums come from the matrix core too: an all-ones A operand turns
+    // P^T into its column sums.
+    auto accumulate = [&](auto SV) {
+        const unsigned char *base = vbuf[0] + decltype(SV)::value * TILE;
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const unsigned char *p = base + pc * 32 * ROWB + vofs[db];
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWB));
+                const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const vec8 a = __builtin_bit_cast(vec8, both);
+                oacc[db][0] = Mfma<T>::run(a, pb[pc][0], oacc[db][0]);
+                oacc[db][1] = Mfma<T>::run(a, pb[pc][1], oacc[db][1]);
+            }
+            lacc[0] = Mfma<T>::run(ones, pb[pc][0], lacc[0]);
+            lacc[1] = Mfma<T>::run(ones, pb[pc][1], lacc[1]);
+        }        pin_acc();
+    };
+
+    // ---- online softmax of tile j with lazy rescaling ----------------------------
+    // The running max m only moves when a row's tile max exceeds it by more
+    // than 8 (base 2); otherwise the stale m is kept, so the probabilities
+    // stay <= 2^8 and the accumulator needs no rescale.  The result is
+    // unchanged: O and l share the same m.
+    auto softmax = [&](const int j) {
+        const int j0 = j * kBC;
+        if (j0 + kBC > full_end) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int t = lim[qb] - j0;
@@ -267,12 +338,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
                         if (kb * 16 + r > t) s[kb][qb][r] = -INFINITY;
             }
         }
-
-        // ---- online softmax with lazy rescaling ------------------------------
-        // The running max m only moves when a row's tile max exceeds it by
-        // more than 8 (base 2); otherwise the stale m is kept, so the
-        // probabilities stay <= 2^8 and the accumulator needs no rescale.
-        // The result is unchanged: O and l share the same m.
         float mt[2];
         bool need[2];
 #pragma unroll
@@ -291,13 +356,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
                 const float m_new = need[qb] ? mt[qb] : m[qb];
                 const float alpha = fast_exp2(m[qb] - m_new);   // 0 when m = -inf < m_new
                 const float a = need[qb] ? alpha : 1.f;
-                l[qb] *= a;
+                lacc[qb] *= a;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[db][qb] *= a;
                 m[qb] = m_new;
             }
         }
-        vec8 pb[PC][2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const float m_use = (m[qb] == -INFINITY) ? 0.f : m[qb];
@@ -309,60 +373,124 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         pf[4 * h + r] = fast_exp2(fmaf(s[2 * pc + h][qb][r], c, -m_use));
-                const vec8 t = __builtin_convertvector(pf, vec8);
-                pb[pc][qb] = t;
-                l[qb] = row_sum_pairs(t, l[qb]);
+                pb[pc][qb] = __builtin_convertvector(pf, vec8);
             }
-        }
-
-        // ---- O^T += V^T P^T ------------------------------------------------
-        const unsigned char *vs_base = smem[buf][1];
-#pragma unroll
-        for (int pc = 0; pc < PC; ++pc) {
-            {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int r_lo = pc * 32 + 4 * g + li / 4;
-                    const int r_hi = r_lo + 16;
-                    const int u = 4 * db + (li % 4);
-                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                    lds_i16x4 *p_lo = (lds_i16x4 *)(vs_base + r_lo * ROWB + ((u ^ vswz<D>(r_lo)) * 8));
-                    lds_i16x4 *p_hi = (lds_i16x4 *)(vs_base + r_hi * ROWB + ((u ^ vswz<D>(r_hi)) * 8));
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p_lo);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p_hi);
-                    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    const vec8 a = __builtin_bit_cast(vec8, both);
-                    oacc[db][0] = Mfma<T>::run(a, pb[pc][0], oacc[db][0]);
-                    oacc[db][1] = Mfma<T>::run(a, pb[pc][1], oacc[db][1]);
-                }
-            }
-        }
+        }        pin_probs();
+        pin_acc();
     };
 
-    // Tile j is waited for (this wave's loads via vmcnt, everyone's via the
-    // barrier, which also frees the stage tile j-1 used), then tile
-    // j+NBUF-1 is issued into that freed stage, then tile j is consumed.
-    // The explicit wait leaves the loads of the NBUF-2 later tiles in flight.
-#pragma unroll
-    for (int p = 0; p < NBUF - 1; ++p) issue(p);
-    // Re-define the Q operands here so that the loop carries no dependence on
-    // their loads (the loop would otherwise wait for every outstanding load).
+    // ---- ping-pong schedule ------------------------------------------------------
+    // Time is cut into intervals by workgroup barriers.  Group A forms the
+    // scores of tile j and adds P V of tile j-1 (matrix cores) while group B
+    // turns the scores of tile j-1 into probabilities (vector ALU); in the
+    // next interval the roles swap.  The two waves sharing a SIMD thus keep
+    // the matrix core and the vector ALU busy at the same time.  Both groups
+    // pass the same number of barriers: B starts with one, A ends with one.
+    //
+    // Loads: K tiles 0-2 and V tiles 0-1 are fetched up front.  Load step i
+    // (the barrier after group A's softmax of tile i) waits until K tile
+    // i+1 and V tile i have landed, then fetches K tile i+3 and V tile i+2
+    // into the stages of K tile i and V tile i-1, whose last readers (group
+    // B's interval before that barrier) are done.  Only tiles below ntiles
+    // are loaded, so nothing is in flight once the item ends.
+    // Workgroup barrier that the compiler may not schedule work across, so
+    // that each phase's instructions stay inside its interval.
+    auto phase_barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto load_step = [&](const int i) {
+        if (i + 2 < ntiles) wait_vmcnt<2 * LPT>();
+        else if (i + 1 < ntiles) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+        phase_barrier();
+        issue_k(i + 3);
+        issue_v(i + 2);
+    };
+    // The stage of tile j is j % 3 for K and V alike; the loop bodies are
+    // specialised per stage so that every LDS address is a per-lane register
+    // plus an immediate offset.
+    typedef std::integral_constant<int, 0> S0;
+    typedef std::integral_constant<int, 1> S1;
+    typedef std::integral_constant<int, 2> S2;
+    auto with_stage = [&](const int j, auto f) {
+        const int r = j % 3;
+        if (r == 0) f(S0{});
+        else if (r == 1) f(S1{});
+        else f(S2{});
+    };
+    issue_k(0);
+    issue_k(1);
+    issue_v(0);
+    issue_k(2);
+    issue_v(1);
+    wait_vmcnt<0>();
+    // Re-define the Q operands here so that the loops carry no dependence on
+    // their loads (they would otherwise wait for every outstanding load).
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[qb][ks]));
-    for (int j = 0; j < ntiles; ++j) {
-        wait_vmcnt<2 * LPT * (NBUF - 2)>();
-        __builtin_amdgcn_s_barrier();
-        issue(j + NBUF - 1);
-        const int j0 = j * kBC;
-        tile(j % NBUF, j0, j0 + kBC > full_end);
+    phase_barrier();
+    if (grp == 0) {
+        if (wtiles > 0) scores(S0{});
+        phase_barrier();
+        if (wtiles > 0) softmax(0);
+        load_step(0);
+        // Steady state, tile j in stage j % 3 (j starts at 1): unrolled by
+        // three so that no stage switch merges register assignments.
+        auto body = [&](const int j, auto R) {
+            accumulate(std::integral_constant<int, (decltype(R)::value + 2) % 3>{});
+            scores(R);
+            phase_barrier();
+            softmax(j);
+            load_step(j);
+        };
+        int j = 1;
+        for (; j + 3 <= wtiles; j += 3) {
+            body(j, S1{});
+            body(j + 1, S2{});
+            body(j + 2, S0{});
+        }
+        if (j < wtiles) body(j++, S1{});
+        if (j < wtiles) body(j++, S2{});
+        for (; j <= ntiles; ++j) {
+            if (j == wtiles) with_stage(j - 1, [&](auto R) { accumulate(R); });
+            phase_barrier();
+            load_step(j);
+        }
+    } else {
+        phase_barrier();
+        if (wtiles > 0) scores(S0{});
+        load_step(0);
+        if (wtiles > 0) softmax(0);
+        auto body = [&](const int j, auto R) {
+            phase_barrier();
+            accumulate(std::integral_constant<int, (decltype(R)::value + 2) % 3>{});
+            scores(R);
+            load_step(j);
+            softmax(j);
+        };
+        int j = 1;
+        for (; j + 3 <= wtiles; j += 3) {
+            body(j, S1{});
+            body(j + 1, S2{});
+            body(j + 2, S0{});
+        }
+        if (j < wtiles) body(j++, S1{});
+        if (j < wtiles) body(j++, S2{});
+        for (; j <= ntiles; ++j) {
+            phase_barrier();
+            if (j == wtiles) with_stage(j - 1, [&](auto R) { accumulate(R); });
+            load_step(j);
+        }
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const float lt = rows_sum(l[qb]);
+        const float lt = lacc[qb][0];
         const int qi = qw0 + qb * 16 + li;
         if (qi >= N) continue;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -377,16 +505,41 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void fwd_mfma_kernel(
         }
         if (g == 0) lse[(int64_t)head * N + qi] = lt > 0.f ? (m[qb] + fast_log2(lt)) * kLn2 : -INFINITY;
     }
+    }   // item loop
+}
+
+// Resident workgroups per CU of one kernel instantiation, times the CU count
+// of the current device (cached per device).
+template <typename T, int D, bool CAUSAL>
+int resident_workgroups() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&fwd_mfma_kernel<T, D, CAUSAL>), kThreads, 0) !=
+        hipSuccess)
+        return 0;
+    v = cus * (per_cu > 0 ? per_cu : 1);
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    return v;
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch3(const FwdArgs &a) {
     const int q_blocks = (int)((a.N + kBR - 1) / kBR);
-    const int64_t num_wg = a.B * a.H * q_blocks;
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL>), dim3((unsigned)num_wg), dim3(kThreads), 0,
+    const int64_t n_items = a.B * a.H * q_blocks;
+    const int resident = resident_workgroups<T, D, CAUSAL>();
+    if (resident <= 0) return hipErrorInvalidDevice;
+    const int64_t grid = n_items < resident ? n_items : resident;
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                        a.stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<T *>(a.o), a.lse, (int)a.N,
-                       (int)a.Nk, a.scale * kLog2e, q_blocks, (int)num_wg);
+                       (int)a.Nk, a.scale * kLog2e, q_blocks, (int)n_items);
     return hipGetLastError();
 }
 
