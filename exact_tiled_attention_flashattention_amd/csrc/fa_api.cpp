@@ -105,8 +105,9 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, void *o, float *
     if (st != FA_OK) return st;
     fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, stream);
     (void)hipGetLastError();   // clear any stale error so it is not reported as ours
-    hipError_t e = fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_mfma(a)
-                                                          : fa::launch_fwd_rowwise(a);
+    hipError_t e = !fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_rowwise(a)
+                   : d == 64                                    ? fa::launch_fwd_mfma_d64(a)
+                                                                : fa::launch_fwd_mfma_d128(a);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -1,6 +1,7 @@
 // fa_fwd_mfma.hip -- exact attention forward on the CDNA4 matrix cores.
 //
-// bf16/fp16 inputs, d == dv in {64, 128}, scale > 0; fp32 accumulation.
+// bf16/fp16 inputs, d == dv == 64, scale > 0; fp32 accumulation.  (d = 128
+// runs on the variant in fa_fwd_mfma_wide.hip.)
 //
 // Method: the FlashAttention-2 loop order of CS349E Lecture 11
 // "flash_lab.py", section 3 (flash_fwd, order "fa2"): one block of 256
@@ -550,7 +551,7 @@ hipError_t launch2(const FwdArgs &a) {
 
 template <typename T>
 hipError_t launch1(const FwdArgs &a) {
-    return a.d == 64 ? launch2<T, 64>(a) : launch2<T, 128>(a);
+    return launch2<T, 64>(a);
 }
 
 }  // namespace
@@ -559,7 +560,7 @@ bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale) {
     return (dtype == kBF16 || dtype == kF16) && d == dv && (d == 64 || d == 128) && scale > 0.f;
 }
 
-hipError_t launch_fwd_mfma(const FwdArgs &a) {
+hipError_t launch_fwd_mfma_d64(const FwdArgs &a) {
     return a.dtype == kBF16 ? launch1<bf16_t>(a) : launch1<f16_t>(a);
 }
 

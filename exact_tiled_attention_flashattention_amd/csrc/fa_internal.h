@@ -38,7 +38,8 @@ hipError_t launch_fwd_rowwise(const FwdArgs &a);
 
 // MFMA forward for bf16/fp16 with d == dv in {64, 128} and scale > 0.
 bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale);
-hipError_t launch_fwd_mfma(const FwdArgs &a);
+hipError_t launch_fwd_mfma_d64(const FwdArgs &a);    // fa_fwd_mfma.hip
+hipError_t launch_fwd_mfma_d128(const FwdArgs &a);   // fa_fwd_mfma_wide.hip
 
 // Split-KV decode: segment kernel then merge kernel, same stream.
 hipError_t launch_decode_splitkv(const DecodeArgs &a);
