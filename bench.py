@@ -217,6 +217,60 @@ def summarize_trace(directory: str) -> None:
         print("\n".join(lines))
 
 
+GQA = dict(B=8, Hq=32, Hkv=8, Nk=32768, d=128, num_splits=64, seed_q=41, seed_kv=42)
+
+
+def bench_gqa(args, torch, fa, si, dev) -> int:
+    """Grouped-query split-KV decode: 4 query heads per key/value head, the
+    long-context decode size with 8 key/value heads.  Algorithmic bytes are K
+    and V once per key/value head plus Q, O (bf16) and LSE (fp32)."""
+    g = GQA
+    q, _, _ = si.device_qkv(si.Shape(g["B"], g["Hq"], 1, 1, g["d"], g["d"]), g["seed_q"], "bf16", dev)
+    _, k, v = si.device_qkv(si.Shape(g["B"], g["Hkv"], 1, g["Nk"], g["d"], g["d"]), g["seed_kv"],
+                            "bf16", dev)
+    o = torch.empty((g["B"], g["Hq"], 1, g["d"]), dtype=q.dtype, device=dev)
+    lse = torch.empty((g["B"], g["Hq"], 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_splitkv_workspace_size(g["B"], g["Hq"], 1, g["d"], g["num_splits"]),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        fa.decode_splitkv_gqa(q, k, v, num_splits=g["num_splits"], workspace=ws, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i].record(stream)
+        call()
+    ev[args.steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    avg_s = sum(ms) / len(ms) / 1e3
+    e = 2
+    nbytes = (g["B"] * g["Hkv"] * 2 * g["Nk"] * g["d"] * e
+              + g["B"] * g["Hq"] * (2 * g["d"] * e + 4))
+    gbs = nbytes / avg_s / 1e9
+    print(json.dumps({
+        "metric": "GQA split-KV decode HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded torch Philox draws on the GPU)",
+        "config": {"workload": "decode_gqa_b8_hq32_hkv8_nk32768_d128", **{k2: v2 for k2, v2 in g.items()
+                                                                        if not k2.startswith("seed")}},
+        "roofline": {"kernel": "decode_segment_kernel<bf16,128,4> + decode_merge_kernel",
+                     "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(avg_s * 1e6, 2), "min_launch_us": round(min(ms) * 1e3, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,8 +281,9 @@ def main() -> int:
                     help="prefill heads the CPU oracle is timed on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="add one plain 1 GiB device copy per step (for counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode"],
-                    help="profile one entry point alone (the JSON line then omits the other)")
+    ap.add_argument("--only", choices=["prefill", "decode", "gqa"],
+                    help="profile one entry point alone (the JSON line then omits the other); "
+                         "'gqa' times the grouped-query decode (not part of the default line)")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
     args = ap.parse_args()
@@ -255,6 +310,8 @@ def main() -> int:
 
     fa.library()   # fail loudly here if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.only == "gqa":
+        return bench_gqa(args, torch, fa, si, dev)
     wp = si.WORKLOADS[PREFILL]
     wd = si.WORKLOADS[DECODE]
     sp, sd = wp.shapes[0], wd.shapes[0]

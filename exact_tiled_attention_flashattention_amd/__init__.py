@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = [
-    "fwd", "decode_splitkv", "decode_splitkv_workspace_size", "status_string",
+    "fwd", "decode_splitkv", "decode_splitkv_gqa", "decode_splitkv_workspace_size", "status_string",
     "FAError", "library", "LIBRARY_PATH", "FA_OK", "FA_ERR_INVALID_ARG",
     "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
 ]
@@ -57,6 +57,10 @@ def library() -> ctypes.CDLL:
     lib.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, c_int,
                                       ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t, vp]
     lib.fa_decode_splitkv.restype = c_int
+    lib.fa_decode_splitkv_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                          c_int, ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t,
+                                          vp]
+    lib.fa_decode_splitkv_gqa.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -67,7 +71,7 @@ def status_string(status: int) -> str:
     return library().fa_status_string(int(status)).decode()
 
 
-def _check_qkv(q, k, v):
+def _check_qkv(q, k, v, grouped=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -82,8 +86,14 @@ def _check_qkv(q, k, v):
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
     B, H, N, d = q.shape
-    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != d or v.shape[2] != k.shape[2]:
+    Hkv = k.shape[1]
+    bad = (k.shape[0] != B or v.shape[:2] != k.shape[:2] or k.shape[3] != d
+           or v.shape[2] != k.shape[2])
+    bad = bad or (Hkv != H if not grouped else (Hkv < 1 or H % Hkv != 0))
+    if bad:
         raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if grouped:
+        return B, H, Hkv, N, k.shape[2], d, v.shape[3]
     return B, H, N, k.shape[2], d, v.shape[3]
 
 
@@ -150,4 +160,35 @@ def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
                                      _stream_handle(q.device, stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_splitkv")
+    return out, lse
+
+
+def decode_splitkv_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+                       scale: float | None = None, num_splits: int = 64,
+                       workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                       lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Grouped-query split-KV decoding through ``fa_decode_splitkv_gqa``.
+
+    q [B,Hq,N,d]; k [B,Hkv,Nk,d], v [B,Hkv,Nk,dv] with Hq a multiple of Hkv;
+    query head h uses key/value head h // (Hq // Hkv).  Returns ``(o, lse)``
+    like :func:`decode_splitkv`.
+    """
+    B, Hq, Hkv, N, Nk, d, dv = _check_qkv(q, k, v, grouped=True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = decode_splitkv_workspace_size(B, Hq, N, dv, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = library().fa_decode_splitkv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         lse.data_ptr(), B, Hq, Hkv, N, Nk, d, dv,
+                                         int(bool(causal)), float(scale), _DTYPE_CODE[q.dtype],
+                                         int(num_splits), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(q.device, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_splitkv_gqa")
     return out, lse

@@ -122,28 +122,58 @@ size_t fa_decode_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t
     return static_cast<size_t>(x);
 }
 
+}  // extern "C"
+
+namespace {
+
+fa_status_t decode_impl(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk, int64_t d,
+                        int64_t dv, int causal, float scale, fa_dtype_t dtype, int num_splits,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (num_splits < 1) return FA_ERR_INVALID_ARG;
+    if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+    fa_status_t st = check_common(q, k, v, o, lse, B, Hq, N, Nk, d, dv, scale, dtype);
+    if (st != FA_OK) return st;
+    // Launch-shape limits of the segment kernel: (segment, key/value head,
+    // row group of up to 8 of the (Hq / Hkv) x N rows).
+    const int64_t rows = (Hq / Hkv) * N;
+    if (B * Hkv > 65535 || (rows + 7) / 8 > 65535 || rows > kMaxI32 || num_splits > kMaxSplits)
+        return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_decode_splitkv_workspace_size(B, Hq, N, dv, num_splits);
+    if (need == 0) return FA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    fa::DecodeArgs dargs;
+    dargs.a = make_args(q, k, v, o, lse, B, Hq, N, Nk, d, dv, causal, scale, dtype, stream);
+    dargs.Hkv = Hkv;
+    dargs.num_splits = num_splits;
+    dargs.seg_len = segment_length(Nk, num_splits);
+    dargs.ws_o = static_cast<float *>(workspace);
+    dargs.ws_lse = dargs.ws_o + B * Hq * (int64_t)num_splits * N * dv;
+    (void)hipGetLastError();
+    hipError_t e = fa::launch_decode_splitkv(dargs);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
 fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
                               int64_t B, int64_t H, int64_t N, int64_t Nk, int64_t d,
                               int64_t dv, int causal, float scale, fa_dtype_t dtype,
                               int num_splits, void *workspace, size_t workspace_bytes,
                               void *stream) {
-    if (num_splits < 1) return FA_ERR_INVALID_ARG;
-    fa_status_t st = check_common(q, k, v, o, lse, B, H, N, Nk, d, dv, scale, dtype);
-    if (st != FA_OK) return st;
-    // Launch-shape limits of the segment kernel: (segment, head, row group).
-    if (B * H > 65535 || (N + 3) / 4 > 65535 || num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
-    const size_t need = fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits);
-    if (need == 0) return FA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
-    fa::DecodeArgs dargs;
-    dargs.a = make_args(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, stream);
-    dargs.num_splits = num_splits;
-    dargs.seg_len = segment_length(Nk, num_splits);
-    dargs.ws_o = static_cast<float *>(workspace);
-    dargs.ws_lse = dargs.ws_o + B * H * (int64_t)num_splits * N * dv;
-    (void)hipGetLastError();
-    hipError_t e = fa::launch_decode_splitkv(dargs);
-    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return decode_impl(q, k, v, o, lse, B, H, H, N, Nk, d, dv, causal, scale, dtype, num_splits,
+                       workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, void *o,
+                                  float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                  int64_t Nk, int64_t d, int64_t dv, int causal, float scale,
+                                  fa_dtype_t dtype, int num_splits, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return decode_impl(q, k, v, o, lse, B, Hq, Hkv, N, Nk, d, dv, causal, scale, dtype,
+                       num_splits, workspace, workspace_bytes, stream);
 }
 
 const char *fa_status_string(fa_status_t status) {

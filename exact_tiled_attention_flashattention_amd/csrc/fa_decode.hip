@@ -11,8 +11,13 @@
 // workgroup ordering (the partial-buffer pattern the lecture series uses
 // to avoid racing writers).
 //
-// Segment kernel mapping (one workgroup of 4 waves per (segment, head, row
-// group)): a key row of D elements is read as 16-byte pieces by LPK
+// Grouped-query attention (several query heads sharing one key/value head,
+// the packing the lecture recommends for decode): a workgroup serves rows
+// of all G query heads of its key/value head, so K and V are read once per
+// group instead of once per query head.
+//
+// Segment kernel mapping (one workgroup of 4 waves per (segment, key/value
+// head, row group), rows counted over the G query heads x N queries): a key row of D elements is read as 16-byte pieces by LPK
 // consecutive lanes (bf16/fp16 d=128: 16 lanes), so one load instruction of
 // a wave covers KPL = 64/LPK consecutive keys -- a contiguous 1 KiB of K or
 // V.  Each "key slot" (group of LPK lanes) keeps its own online-softmax
@@ -38,7 +43,7 @@ template <typename T, int D, int R>
 __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int N, int Nk, int causal,
-    float scale_log2, int num_splits, int seg_len) {
+    float scale_log2, int num_splits, int seg_len, int G) {
     constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte piece
     constexpr int LPK = D / EPL;               // lanes per key row
     constexpr int KPL = 64 / LPK;              // keys per wave load
@@ -46,27 +51,30 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "bad key-row split");
 
     const int split = blockIdx.x;
-    const int head = blockIdx.y;
-    const int row0 = blockIdx.z * R;
+    const int kvh = blockIdx.y;          // key/value head (over B x Hkv)
+    const int row0 = blockIdx.z * R;     // first row of the group, over G x N
     const int tid = threadIdx.x;
     const int wave = tid / 64;
     const int lane = tid % 64;
     const int slot = lane / LPK;   // which key of a wave load this lane serves
     const int t = lane % LPK;      // which 16-byte piece of the row
 
-    const T *qh = q + (int64_t)head * N * D;
-    const T *kh = k + (int64_t)head * Nk * D;
-    const T *vh = v + (int64_t)head * Nk * D;
+    const T *kh = k + (int64_t)kvh * Nk * D;
+    const T *vh = v + (int64_t)kvh * Nk * D;
 
-    // Query pieces of the R rows served by this workgroup (rows >= N: zero).
+    // Query pieces of the R rows served by this workgroup.  Row x of the
+    // group is query x % N of query head kvh * G + x / N; rows past G * N
+    // are zero and see no key.
     float qr[R][EPL];
     int limit[R];   // last key index visible to each row
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int row = row0 + r;
-        const bool ok = row < N;
+        const int x = row0 + r;
+        const bool ok = x < G * N;
+        const int row = ok ? x % N : 0;
+        const int64_t qhead = (int64_t)kvh * G + (ok ? x / N : 0);
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (ok) raw = *reinterpret_cast<const u32x4 *>(qh + (int64_t)row * D + t * EPL);
+        if (ok) raw = *reinterpret_cast<const u32x4 *>(q + (qhead * N + row) * D + t * EPL);
         const T *e = reinterpret_cast<const T *>(&raw);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) qr[r][i] = to_f32(e[i]);
@@ -153,8 +161,10 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     for (int idx = tid; idx < R * D; idx += kThreads) {
         const int r = idx / D;
         const int c = idx % D;
-        const int row = row0 + r;
-        if (row >= N) continue;
+        const int x = row0 + r;
+        if (x >= G * N) continue;
+        const int row = x % N;
+        const int64_t qhead = (int64_t)kvh * G + x / N;
         float mm = -INFINITY;
         for (int st = 0; st < STATES; ++st) mm = fmaxf(mm, sm_m[r][st]);
         float ll = 0.f, oo = 0.f;
@@ -166,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
                 oo = fmaf(sm_o[r][st][c], f, oo);
             }
         }
-        // Workspace layout: o_s [B*H, S, N, D], lse_s [B*H, S, N].
-        const int64_t part = ((int64_t)head * num_splits + split) * N + row;
+        // Workspace layout: o_s [B*Hq, S, N, D], lse_s [B*Hq, S, N].
+        const int64_t part = (qhead * num_splits + split) * N + row;
         ws_o[part * D + c] = ll > 0.f ? oo / ll : 0.f;
         if (c == 0) ws_lse[part] = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
     }
@@ -249,12 +259,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(
 template <typename T, int D, int R>
 hipError_t launch_rows(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
-    const int64_t groups = (a.N + R - 1) / R;
-    dim3 grid((unsigned)d.num_splits, (unsigned)(a.B * a.H), (unsigned)groups);
+    const int G = (int)(a.H / d.Hkv);
+    const int64_t groups = ((int64_t)G * a.N + R - 1) / R;
+    dim3 grid((unsigned)d.num_splits, (unsigned)(a.B * d.Hkv), (unsigned)groups);
     hipLaunchKernelGGL((decode_segment_kernel<T, D, R>), grid, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), d.ws_o, d.ws_lse, (int)a.N, (int)a.Nk,
-                       a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len);
+                       a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len, G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)),
@@ -264,10 +275,15 @@ hipError_t launch_rows(const DecodeArgs &d) {
     return hipGetLastError();
 }
 
+// Rows per workgroup: the smallest of 1, 2, 4, 8 that covers the G x N rows
+// of a key/value head (8 at most; more rows take more workgroups).
 template <typename T, int D>
 hipError_t launch_dim(const DecodeArgs &d) {
-    if (d.a.N == 1) return launch_rows<T, D, 1>(d);
-    return launch_rows<T, D, 4>(d);
+    const int64_t rows = (d.a.H / d.Hkv) * d.a.N;
+    if (rows == 1) return launch_rows<T, D, 1>(d);
+    if (rows == 2) return launch_rows<T, D, 2>(d);
+    if (rows <= 4) return launch_rows<T, D, 4>(d);
+    return launch_rows<T, D, 8>(d);
 }
 
 template <typename T>

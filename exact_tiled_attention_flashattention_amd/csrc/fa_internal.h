@@ -26,10 +26,11 @@ struct FwdArgs {
 };
 
 struct DecodeArgs {
-    FwdArgs a;
+    FwdArgs a;            // a.H is the number of query heads
+    int64_t Hkv;          // key/value heads; query head h reads key/value head h / (a.H / Hkv)
     int num_splits;
     int64_t seg_len;      // keys per segment (multiple of 64)
-    float *ws_o;          // [B, H, num_splits, N, dv]
+    float *ws_o;          // [B, H, num_splits, N, dv] (H query heads)
     float *ws_lse;        // [B, H, num_splits, N]
 };
 

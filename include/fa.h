@@ -137,6 +137,30 @@ fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void 
                               int num_splits, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/*
+ * fa_decode_splitkv_gqa -- fa_decode_splitkv for grouped-query attention: Hq
+ * query heads share Hkv key/value heads (Hq a multiple of Hkv), query head h
+ * attending with key/value head h / (Hq / Hkv).  The result is that of
+ * fa_fwd on K and V with each key/value head repeated Hq / Hkv times.  Each
+ * workgroup serves the rows of all query heads of one key/value head, so K
+ * and V are read once per group -- the packing flash_lab.py section 4 names
+ * for grouped heads in decode.  fa_decode_splitkv is this call with
+ * Hkv == Hq.
+ *
+ *   q, o      [B, Hq, N, d] and [B, Hq, N, dv]; lse [B, Hq, N].
+ *   k, v      [B, Hkv, Nk, d] and [B, Hkv, Nk, dv].
+ *   Hq, Hkv   query and key/value heads (>= 1, Hq % Hkv == 0, else
+ *             FA_ERR_INVALID_ARG; B * Hkv > 65535: FA_ERR_UNSUPPORTED).
+ *   workspace at least fa_decode_splitkv_workspace_size(B, Hq, N, dv,
+ *             num_splits) bytes (partials are kept per query head).
+ *   all else  as for fa_decode_splitkv.
+ */
+fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, void *o,
+                                  float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                  int64_t Nk, int64_t d, int64_t dv, int causal, float scale,
+                                  fa_dtype_t dtype, int num_splits, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* fa_status_string -- a static, human-readable name of a status code. */
 const char *fa_status_string(fa_status_t status);
 

@@ -25,8 +25,9 @@ def _declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_decode_splitkv", "fa_decode_splitkv_workspace_size",
-                                     "fa_fwd", "fa_status_string"]
+    assert _declared_functions() == ["fa_decode_splitkv", "fa_decode_splitkv_gqa",
+                                     "fa_decode_splitkv_workspace_size", "fa_fwd",
+                                     "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -122,6 +123,31 @@ def test_decode_rejects(kw, expect):
     assert _dec(**kw) == expect
 
 
+def _gqa(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, N=1, Nk=64, d=64, dv=64, causal=0,
+         scale=0.125, dtype=2, ns=4, ws=A, wsb=1 << 20):
+    return fa.library().fa_decode_splitkv_gqa(q, k, v, o, lse, B, Hq, Hkv, N, Nk, d, dv, causal,
+                                              scale, dtype, ns, ws, wsb, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),     # not a multiple
+    (dict(Hq=2, Hkv=4), fa.FA_ERR_INVALID_ARG),     # fewer query than key/value heads
+    (dict(ns=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=256, Hq=512, Hkv=256), fa.FA_ERR_UNSUPPORTED),   # B * Hkv > 65535
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    # the workspace is sized by query heads: 1 x 4 x 4 splits x 1 x 65 x 4 bytes
+    (dict(wsb=4 * 4 * 65 * 4 - 1), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_gqa_rejects(kw, expect):
+    assert _gqa(**kw) == expect
+
+
 def test_binding_requires_gpu_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 64)
@@ -129,3 +155,5 @@ def test_binding_requires_gpu_tensors():
         fa.fwd(x, x, x)
     with pytest.raises(ValueError):
         fa.decode_splitkv(x, x, x)
+    with pytest.raises(ValueError):
+        fa.decode_splitkv_gqa(x, x, x)

@@ -74,3 +74,70 @@ def test_decode_b8_h32_nk32768_d128_sampled_heads():
     l_s = torch.stack([lse[b, h] for b, h in heads])
     compare(o_s, l_s, o_ref, l_ref, w.dtype, w.name)
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+# ---- grouped-query decode (fa_decode_splitkv_gqa) ---------------------------
+# The definition: query head h attends with key/value head h // G, i.e.
+# standard attention on K and V with each key/value head repeated G times.
+
+def _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, num_splits, seed=0, std=1.0):
+    Hq = Hkv * G
+    q, _, _ = make_inputs(B, Hq, N, 1, d, d, dtype, seed, std)
+    _, k, v = make_inputs(B, Hkv, 1, Nk, d, d, dtype, seed + 1000, std)
+    scale = default_scale(d)
+    log(f"fa_decode_splitkv_gqa dtype={dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} Nk={Nk} d={d} "
+        f"causal={causal} splits={num_splits} seed={seed}")
+    o, lse = fa.decode_splitkv_gqa(q, k, v, causal=causal, scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    k_rep = k.repeat_interleave(G, dim=1).contiguous()
+    v_rep = v.repeat_interleave(G, dim=1).contiguous()
+    o_ref, l_ref = oracle_on(q, k_rep, v_rep, causal, scale)
+    compare(o, lse, o_ref, l_ref, dtype, f"gqa {dtype} {B}x{Hq}/{Hkv}x{N}x{Nk}x{d} S={num_splits}")
+    return q, k, v, o, lse
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [2, 3, 4, 8])
+@pytest.mark.parametrize("N", [1, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa(dtype, G, N, causal):
+    _run_gqa(2, 2, G, N, 700, 128 if dtype == "bf16" else 64, dtype, causal, 8, seed=G * 10 + N)
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_gqa_many_rows_per_group(d):
+    # 16 query heads per key/value head and 5 rows each: 80 rows, 10 row groups of 8
+    _run_gqa(1, 2, 16, 5, 333, d, "bf16", True, 3, seed=d)
+
+
+def test_gqa_with_one_group_is_plain_decode():
+    q, k, v = make_inputs(2, 4, 1, 3000, 128, 128, "bf16", 23)
+    o1, l1 = fa.decode_splitkv(q, k, v, num_splits=16)
+    o2, l2 = fa.decode_splitkv_gqa(q, k, v, num_splits=16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_gqa_b8_hq32_hkv8_nk32768_d128_sampled_heads():
+    """Grouped-query decode at the long-context size (4 query heads per
+    key/value head, 64 splits); the oracle checks eight whole query heads."""
+    B, Hq, Hkv, Nk, d = 8, 32, 8, 32768, 128
+    G = Hq // Hkv
+    log(f"fa_decode_splitkv_gqa full-size B={B} Hq={Hq} Hkv={Hkv} Nk={Nk} d={d}")
+    q, _, _ = si.device_qkv(si.Shape(B, Hq, 1, 1, d, d), 31, "bf16", "cuda", 1.0)
+    _, k, v = si.device_qkv(si.Shape(B, Hkv, 1, Nk, d, d), 32, "bf16", "cuda", 1.0)
+    o, lse = fa.decode_splitkv_gqa(q, k, v, num_splits=64)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (B - 1, Hq - 1), (3, 17), (5, 2), (1, 30), (6, 9), (2, 3), (7, 16)]
+    os_, ls_ = [], []
+    for b, h in heads:
+        o_r, l_r = oracle_on(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1],
+                             v[b:b + 1, h // G:h // G + 1], False, default_scale(d))
+        os_.append(o_r[0, 0])
+        ls_.append(l_r[0, 0])
+    import numpy as np
+    o_ref, l_ref = np.stack(os_), np.stack(ls_)
+    o_s = torch.stack([o[b, h] for b, h in heads])
+    l_s = torch.stack([lse[b, h] for b, h in heads])
+    compare(o_s, l_s, o_ref, l_ref, "bf16", "gqa full-size")
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
