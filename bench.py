@@ -195,15 +195,26 @@ def summarize_trace(directory: str) -> None:
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {directory}")
     rows = list(csv.DictReader(open(paths[0])))
-    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
-           "python $R/bench.py --no-cpu-baseline   (run from /tmp, repo at $R; 50 timed + 10 "
-           "warm-up steps, each one fa_fwd and one fa_decode_splitkv call)")
+    default_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
+                   "python $R/bench.py --no-cpu-baseline   (run from /tmp, repo at $R; 50 timed + "
+                   "10 warm-up steps, each one fa_fwd and one fa_decode_splitkv call)")
+    gqa_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_gqa -o run -- "
+               "python $R/bench.py --only gqa   (run from /tmp, repo at $R; 50 timed + 10 warm-up "
+               "fa_decode_splitkv_gqa calls)")
+    # file -> (kernel that must be in the trace, kernels listed, command)
     groups = {
-        f"fwd_mfma_kernel_{PREFILL}.txt": ("fwd_mfma_kernel",),
-        f"decode_splitkv_{DECODE}.txt": ("decode_segment_kernel", "decode_merge_kernel"),
+        f"fwd_mfma_kernel_{PREFILL}.txt": ("fwd_mfma_kernel", ("fwd_mfma_kernel",), default_cmd),
+        f"decode_splitkv_{DECODE}.txt": ("decode_segment_kernel",
+                                         ("decode_segment_kernel", "decode_merge_kernel"),
+                                         default_cmd),
+        f"decode_splitkv_gqa_{GQA_WORKLOAD}.txt": ("decode_segment_mfma_kernel",
+                                                   ("decode_segment_mfma_kernel",
+                                                    "decode_merge_kernel"), gqa_cmd),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for fname, keys in groups.items():
+    for fname, (primary, keys, cmd) in groups.items():
+        if not any(primary in r["Name"] for r in rows):
+            continue
         lines = [f"# rocprofv3 kernel-trace statistics, {fname[:-4]}",
                  f"# command: {cmd}",
                  "# kernel | calls | average us | min us | max us | share of traced GPU time %"]
@@ -218,6 +229,7 @@ def summarize_trace(directory: str) -> None:
 
 
 GQA = dict(B=8, Hq=32, Hkv=8, Nk=32768, d=128, num_splits=64, seed_q=41, seed_kv=42)
+GQA_WORKLOAD = "decode_gqa_b8_hq32_hkv8_nk32768_d128"
 
 
 def bench_gqa(args, torch, fa, si, dev) -> int:
@@ -260,9 +272,9 @@ def bench_gqa(args, torch, fa, si, dev) -> int:
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded torch Philox draws on the GPU)",
-        "config": {"workload": "decode_gqa_b8_hq32_hkv8_nk32768_d128", **{k2: v2 for k2, v2 in g.items()
+        "config": {"workload": GQA_WORKLOAD, **{k2: v2 for k2, v2 in g.items()
                                                                         if not k2.startswith("seed")}},
-        "roofline": {"kernel": "decode_segment_kernel<bf16,128,4> + decode_merge_kernel",
+        "roofline": {"kernel": "decode_segment_mfma_kernel<bf16,128> + decode_merge_kernel",
                      "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "avg_launch_us": round(avg_s * 1e6, 2), "min_launch_us": round(min(ms) * 1e3, 2),

@@ -27,6 +27,8 @@
 // through LDS with the same merge rule.  The loop issues U loads of K and
 // U of V per lane before using them, to keep enough bytes in flight for
 // HBM bandwidth.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
             const uint32_t off = key < seg_end
                                      ? ((uint32_t)key * D + t * EPL) * (uint32_t)sizeof(T)
                                      : kOutOfRange;
-            kraw[u] = buffer_load16(krs, off);
-            vraw[u] = buffer_load16(vrs, off);
+            kraw[u] = buffer_load16_nt(krs, off);
+            vraw[u] = buffer_load16_nt(vrs, off);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -183,70 +185,111 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     }
 }
 
-// One workgroup of 4 waves per (head, row): merge num_splits partial states.
-// Every lane first takes some segments' lse_s to find M = max lse_s and
-// Z = sum exp(lse_s - M) (wave reductions, then across the 4 waves through
-// LDS); then the weights w_s = exp(lse_s - lse) of a chunk of 64 segments
-// are computed once, one per lane, and staged in LDS, and each wave
-// accumulates w_s * o_s over its share of the chunk's segments with the
-// row's columns spread over its lanes; the 4 partial sums meet in LDS.
+// One workgroup of 4 waves per (head, row): merge num_splits partial states
+// with lse = M + ln sum_s e^(lse_s - M) and o = sum_s e^(lse_s - lse) o_s.
+// Each thread folds its share of the lse_s into a running (max, sum) pair;
+// the pairs are combined over the wave with lane exchanges and over the 4
+// waves through LDS.  The partial outputs are summed in chunks of 64
+// segments, 16 per wave, each lane owning D / 64 columns; the loads of the
+// first chunk are issued before the lse reduction, so the whole merge waits
+// on memory about once.
 constexpr int kMergeWaves = 4;
+constexpr int kMergeSpw = 16;   // segments per wave per chunk
+
+__device__ __forceinline__ void lse_fold(float &m, float &z, float x) {
+    if (x == -INFINITY) return;
+    if (x > m) {
+        z = z * expf(m - x) + 1.f;   // m = -inf: z = 0 * 0 + 1
+        m = x;
+    } else {
+        z += expf(x - m);
+    }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse, T *__restrict__ o,
     float *__restrict__ lse, int N, int num_splits) {
     constexpr int CPL = D >= 64 ? D / 64 : 1;      // columns per lane
+    constexpr int CHUNK = kMergeWaves * kMergeSpw;
     const int64_t hr = blockIdx.x;                  // head * N + row
     const int64_t head = hr / N;
     const int row = (int)(hr % N);
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64;
+    const int col0 = lane * CPL;
+    const bool col_ok = col0 < D;
     const int64_t base = head * (int64_t)num_splits * N + row;   // segment s at base + s*N
     __shared__ float red[2][kMergeWaves];
-    __shared__ float wts[64];
+    __shared__ float wts[CHUNK];
     __shared__ float part[kMergeWaves][D];
 
-    float mx = -INFINITY;
-    for (int s = tid; s < num_splits; s += kMergeWaves * 64) mx = fmaxf(mx, ws_lse[base + (int64_t)s * N]);
-    mx = group_max<64>(mx);
-    if (lane == 0) red[0][wave] = mx;
+    float ov[kMergeSpw][CPL];
+    auto load_chunk = [&](int s0) {
+#pragma unroll
+        for (int i = 0; i < kMergeSpw; ++i) {
+            const int s = s0 + wave * kMergeSpw + i;
+            const bool ok = col_ok && s < num_splits;
+            const float *src = ws_o + (base + (int64_t)s * N) * D + col0;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ov[i][c] = ok ? src[c] : 0.f;
+        }
+    };
+    load_chunk(0);
+
+    float mx = -INFINITY, z = 0.f, x0 = -INFINITY;
+    for (int s = tid; s < num_splits; s += kMergeWaves * 64) {
+        const float x = ws_lse[base + (int64_t)s * N];
+        if (s == tid) x0 = x;
+        lse_fold(mx, z, x);
+    }
+    {   // combine (max, sum) over the wave, then over the waves
+        const float wm = group_max<64>(mx);
+        float zz = (mx == -INFINITY) ? 0.f : z * expf(mx - wm);
+        zz = group_sum<64>(zz);
+        if (lane == 0) {
+            red[0][wave] = wm;
+            red[1][wave] = zz;
+        }
+    }
     __syncthreads();
-    mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, red[0][w]);
     T *orow = o + hr * D;
-    if (mx == -INFINITY) {   // no visible key in any segment
+    if (M == -INFINITY) {   // no visible key in any segment
         for (int c = tid; c < D; c += kMergeWaves * 64) orow[c] = from_f32<T>(0.f);
         if (tid == 0) lse[hr] = -INFINITY;
         return;
     }
-    float z = 0.f;
-    for (int s = tid; s < num_splits; s += kMergeWaves * 64) z += expf(ws_lse[base + (int64_t)s * N] - mx);
-    z = group_sum<64>(z);
-    if (lane == 0) red[1][wave] = z;
-    __syncthreads();
-    z = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-    const float total = mx + logf(z);
+    float Z = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w)
+        Z += red[0][w] == -INFINITY ? 0.f : red[1][w] * expf(red[0][w] - M);
+    const float total = M + logf(Z);
 
     float acc[CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-    const int col0 = lane * CPL;
-    for (int s0 = 0; s0 < num_splits; s0 += 64) {
-        const int cnt = min(64, num_splits - s0);
-        __syncthreads();   // previous chunk's weights consumed
-        if (tid < cnt) wts[tid] = expf(ws_lse[base + (int64_t)(s0 + tid) * N] - total);   // 0 if empty
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    for (int s0 = 0; s0 < num_splits; s0 += CHUNK) {
+        if (s0 > 0) {
+            load_chunk(s0);
+            __syncthreads();   // previous chunk's weights consumed
+        }
+        if (tid < CHUNK && s0 + tid < num_splits) {
+            const float x = s0 == 0 ? x0 : ws_lse[base + (int64_t)(s0 + tid) * N];
+            wts[tid] = expf(x - total);   // 0 for an empty segment
+        }
         __syncthreads();
-        if (col0 < D) {
-#pragma unroll 4
-            for (int i = wave; i < cnt; i += kMergeWaves) {
-                const float w = wts[i];
-                const float *src = ws_o + (base + (int64_t)(s0 + i) * N) * D + col0;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w, src[c], acc[c]);
-            }
+        for (int i = 0; i < kMergeSpw; ++i) {
+            const int j = wave * kMergeSpw + i;
+            const float w = s0 + j < num_splits ? wts[j] : 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w, ov[i][c], acc[c]);
         }
     }
-    if (col0 < D) {
+    if (col_ok) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) part[wave][col0 + c] = acc[c];
     }
@@ -257,7 +300,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(
 }
 
 template <typename T, int D, int R>
-hipError_t launch_rows(const DecodeArgs &d) {
+hipError_t launch_segment(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
     const int G = (int)(a.H / d.Hkv);
     const int64_t groups = ((int64_t)G * a.N + R - 1) / R;
@@ -266,24 +309,32 @@ hipError_t launch_rows(const DecodeArgs &d) {
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), d.ws_o, d.ws_lse, (int)a.N, (int)a.Nk,
                        a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len, G);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)),
-                       dim3(kMergeWaves * 64),
-                       0, a.stream, d.ws_o, d.ws_lse, static_cast<T *>(a.o), a.lse, (int)a.N,
-                       d.num_splits);
     return hipGetLastError();
 }
 
-// Rows per workgroup: the smallest of 1, 2, 4, 8 that covers the G x N rows
-// of a key/value head (8 at most; more rows take more workgroups).
+// Segment kernel choice.  bf16/fp16 with at least kMfmaMinRows rows per
+// key/value head (grouped heads, several queries) run on the matrix cores
+// (fa_decode_mfma.hip): there the per-key work grows with the rows and the
+// VALU kernel below would stop being bound by memory.  Otherwise the VALU
+// kernel runs with the smallest of 1, 2, 4, 8 rows per workgroup that
+// covers the rows (8 at most; more rows take more workgroups).
+constexpr int64_t kMfmaMinRows = 2;
+
 template <typename T, int D>
 hipError_t launch_dim(const DecodeArgs &d) {
-    const int64_t rows = (d.a.H / d.Hkv) * d.a.N;
-    if (rows == 1) return launch_rows<T, D, 1>(d);
-    if (rows == 2) return launch_rows<T, D, 2>(d);
-    if (rows <= 4) return launch_rows<T, D, 4>(d);
-    return launch_rows<T, D, 8>(d);
+    const FwdArgs &a = d.a;
+    const int64_t rows = (a.H / d.Hkv) * a.N;
+    hipError_t e;
+    if (!std::is_same<T, float>::value && rows >= kMfmaMinRows) e = launch_decode_segment_mfma(d);
+    else if (rows == 1) e = launch_segment<T, D, 1>(d);
+    else if (rows == 2) e = launch_segment<T, D, 2>(d);
+    else if (rows <= 4) e = launch_segment<T, D, 4>(d);
+    else e = launch_segment<T, D, 8>(d);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)),
+                       dim3(kMergeWaves * 64), 0, a.stream, d.ws_o, d.ws_lse,
+                       static_cast<T *>(a.o), a.lse, (int)a.N, d.num_splits);
+    return hipGetLastError();
 }
 
 template <typename T>

@@ -87,6 +87,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
+// The same load with the non-temporal hint, for data that is read exactly
+// once (the decode K/V stream): it measurably raises streaming bandwidth.
+__device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);
+}
 
 // The same raw buffer resource as four scalar words (for inline assembly).
 __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {

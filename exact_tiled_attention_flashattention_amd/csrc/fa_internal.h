@@ -44,5 +44,7 @@ hipError_t launch_fwd_mfma_d128(const FwdArgs &a);   // fa_fwd_mfma_wide.hip
 
 // Split-KV decode: segment kernel then merge kernel, same stream.
 hipError_t launch_decode_splitkv(const DecodeArgs &a);
+// Matrix-core segment kernel (bf16/fp16), fa_decode_mfma.hip.
+hipError_t launch_decode_segment_mfma(const DecodeArgs &a);
 
 }  // namespace fa

@@ -1,4 +1,6 @@
 """fa_decode_splitkv (through the C ABI) against the FP64 oracle on the GPU."""
+import math
+
 import pytest
 import torch
 
@@ -81,9 +83,14 @@ def test_decode_b8_h32_nk32768_d128_sampled_heads():
 # standard attention on K and V with each key/value head repeated G times.
 
 def _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, num_splits, seed=0, std=1.0):
+    """`std` scales Q and K; V keeps unit scale (dividing by a power of two is
+    exact), so the tolerance on O keeps its meaning."""
     Hq = Hkv * G
     q, _, _ = make_inputs(B, Hq, N, 1, d, d, dtype, seed, std)
     _, k, v = make_inputs(B, Hkv, 1, Nk, d, d, dtype, seed + 1000, std)
+    if std != 1.0:
+        assert std == 2.0 ** round(math.log2(std))
+        v = v / std
     scale = default_scale(d)
     log(f"fa_decode_splitkv_gqa dtype={dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} Nk={Nk} d={d} "
         f"causal={causal} splits={num_splits} seed={seed}")
@@ -108,6 +115,24 @@ def test_gqa(dtype, G, N, causal):
 def test_gqa_many_rows_per_group(d):
     # 16 query heads per key/value head and 5 rows each: 80 rows, 10 row groups of 8
     _run_gqa(1, 2, 16, 5, 333, d, "bf16", True, 3, seed=d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("G,N,Nk,splits,causal", [
+    (4, 1, 1000, 16, False),    # one 16-row tile, 4 rows used
+    (16, 1, 95, 7, True),       # a full tile; ragged last block of 32 keys
+    (2, 8, 70, 40, True),       # most segments empty
+    (5, 4, 3, 2, True),         # N > Nk: row 0 of every head sees no key
+    (6, 3, 515, 5, False),      # 18 rows: two tiles, the second nearly empty
+])
+def test_gqa_matrix_core_shapes(dtype, d, G, N, Nk, splits, causal):
+    _run_gqa(1, 2, G, N, Nk, d, dtype, causal, splits, seed=G + N + d)
+
+
+def test_gqa_large_scores():
+    # scores with standard deviation ~16: the running maximum moves often
+    _run_gqa(2, 2, 4, 1, 2000, 128, "bf16", False, 8, seed=5, std=4.0)
 
 
 def test_gqa_with_one_group_is_plain_decode():
