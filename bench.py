@@ -283,6 +283,83 @@ def bench_gqa(args, torch, fa, si, dev) -> int:
     return 0
 
 
+SPLIT_CANDIDATES = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+SWEEP_FILE = os.path.join(ROOT, "profiles", "decode_split_sweep.txt")
+
+
+def sweep_shapes():
+    """Decode shapes (B, Hq, Hkv, N, Nk, d) of the split-count sweep: plain and
+    grouped heads, one and several queries, short to long contexts; K and V
+    stay under 4 GiB each."""
+    out = []
+    for B, Hq, Hkv in [(1, 8, 8), (1, 32, 32), (4, 32, 32), (16, 32, 32), (64, 32, 32),
+                       (1, 32, 8), (8, 32, 8), (32, 32, 8), (1, 64, 8), (16, 64, 8), (4, 8, 1)]:
+        for Nk in (1024, 4096, 16384, 65536, 262144):
+            for N in (1, 4):
+                if N == 4 and Hq != Hkv:
+                    continue
+                if B * Hkv * Nk * 128 * 2 > (4 << 30):
+                    continue
+                out.append((B, Hq, Hkv, N, Nk, 128))
+    return out
+
+
+def split_sweep(args, torch, fa) -> int:
+    """Time decode at every candidate split count for each sweep shape (HIP
+    events, median of args.steps launches after args.warmup) and write the
+    table that the automatic split rule is checked against."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(7)
+    big = torch.randn(1 << 31, generator=gen, device=dev, dtype=torch.bfloat16)   # 4 GiB
+    bigv = torch.randn(1 << 31, generator=gen, device=dev, dtype=torch.bfloat16)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lines = ["# decode time (us, HIP events, median of %d launches after %d warm-up) per split "
+             "count, bf16, d = 128, non-causal; 'auto' is the split count "
+             "fa_decode_splitkv_auto_splits picks and its time relative to the best" % (
+                 args.steps, args.warmup),
+             "# command: python bench.py --split-sweep --steps %d --warmup %d" % (
+                 args.steps, args.warmup),
+             "# B Hq Hkv N Nk | " + " ".join(f"S={c}" for c in SPLIT_CANDIDATES) +
+             " | best | auto (x best)"]
+    for (B, Hq, Hkv, N, Nk, d) in sweep_shapes():
+        q = torch.randn(B, Hq, N, d, generator=gen, device=dev).to(torch.bfloat16)
+        k = big[:B * Hkv * Nk * d].view(B, Hkv, Nk, d)
+        v = bigv[:B * Hkv * Nk * d].view(B, Hkv, Nk, d)
+        o = torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
+        times = {}
+        for S in SPLIT_CANDIDATES:
+            if S > 1 and (S - 1) * 64 >= Nk:
+                continue
+            if fa.decode_splitkv_workspace_size(B, Hq, N, d, S) > ws.numel():
+                continue
+
+            def call():
+                fa.decode_splitkv_gqa(q, k, v, num_splits=S, workspace=ws, out=o, lse=lse)
+            for _ in range(args.warmup):
+                call()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            for i in range(args.steps):
+                ev[i].record(stream)
+                call()
+            ev[args.steps].record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+            times[S] = ms[len(ms) // 2] * 1e3
+        best = min(times, key=times.get)
+        auto = fa.decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, q.dtype)
+        cells = " ".join(f"{times[c]:.1f}" if c in times else "-" for c in SPLIT_CANDIDATES)
+        rel = times[auto] / times[best] if auto in times else float("nan")
+        line = f"{B} {Hq} {Hkv} {N} {Nk} | {cells} | {best} | {auto} ({rel:.3f})"
+        lines.append(line)
+        print(line, flush=True)
+    os.makedirs(os.path.dirname(SWEEP_FILE), exist_ok=True)
+    with open(SWEEP_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +373,9 @@ def main() -> int:
     ap.add_argument("--only", choices=["prefill", "decode", "gqa"],
                     help="profile one entry point alone (the JSON line then omits the other); "
                          "'gqa' times the grouped-query decode (not part of the default line)")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="time decode at every candidate split count over a set of shapes "
+                         "and write the table under profiles/")
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--summarize-trace", metavar="DIR")
     args = ap.parse_args()
@@ -324,6 +404,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.only == "gqa":
         return bench_gqa(args, torch, fa, si, dev)
+    if args.split_sweep:
+        return split_sweep(args, torch, fa)
     wp = si.WORKLOADS[PREFILL]
     wd = si.WORKLOADS[DECODE]
     sp, sd = wp.shapes[0], wd.shapes[0]

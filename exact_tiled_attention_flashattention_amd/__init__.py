@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = [
-    "fwd", "decode_splitkv", "decode_splitkv_gqa", "decode_splitkv_workspace_size", "status_string",
+    "fwd", "decode_splitkv", "decode_splitkv_gqa", "decode_splitkv_workspace_size",
+    "decode_splitkv_auto_splits", "status_string",
     "FAError", "library", "LIBRARY_PATH", "FA_OK", "FA_ERR_INVALID_ARG",
     "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
 ]
@@ -61,6 +62,8 @@ def library() -> ctypes.CDLL:
                                           c_int, ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t,
                                           vp]
     lib.fa_decode_splitkv_gqa.restype = c_int
+    lib.fa_decode_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, i64, i64, c_int]
+    lib.fa_decode_splitkv_auto_splits.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -132,6 +135,15 @@ def decode_splitkv_workspace_size(B: int, H: int, N: int, dv: int, num_splits: i
     return int(library().fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits))
 
 
+def decode_splitkv_auto_splits(B: int, Hq: int, Hkv: int, N: int, Nk: int, d: int,
+                               dtype: torch.dtype) -> int:
+    """The split count ``num_splits=0`` selects (``fa_decode_splitkv_auto_splits``)."""
+    n = int(library().fa_decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, _DTYPE_CODE[dtype]))
+    if n < 1:
+        raise ValueError(f"no split count for B={B} Hq={Hq} Hkv={Hkv} N={N} Nk={Nk} d={d}")
+    return n
+
+
 def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                    scale: float | None = None, num_splits: int = 64,
                    workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
@@ -142,6 +154,7 @@ def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
     ``num_splits`` segments reduced in parallel, then merged by a second kernel.
     ``workspace`` (a uint8 device tensor of at least
     :func:`decode_splitkv_workspace_size` bytes) is allocated if not given.
+    ``num_splits=0`` lets the library choose (:func:`decode_splitkv_auto_splits`).
     """
     B, H, N, Nk, d, dv = _check_qkv(q, k, v)
     if scale is None:
@@ -151,7 +164,8 @@ def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if workspace is None:
-        nbytes = decode_splitkv_workspace_size(B, H, N, dv, num_splits)
+        splits = num_splits or decode_splitkv_auto_splits(B, H, H, N, Nk, d, q.dtype)
+        nbytes = decode_splitkv_workspace_size(B, H, N, dv, splits)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = library().fa_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                      lse.data_ptr(), B, H, N, Nk, d, dv, int(bool(causal)),
@@ -181,7 +195,8 @@ def decode_splitkv_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     if workspace is None:
-        nbytes = decode_splitkv_workspace_size(B, Hq, N, dv, num_splits)
+        splits = num_splits or decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, q.dtype)
+        nbytes = decode_splitkv_workspace_size(B, Hq, N, dv, splits)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = library().fa_decode_splitkv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          lse.data_ptr(), B, Hq, Hkv, N, Nk, d, dv,

@@ -27,8 +27,6 @@
 // through LDS with the same merge rule.  The loop issues U loads of K and
 // U of V per lane before using them, to keep enough bytes in flight for
 // HBM bandwidth.
-#include <type_traits>
-
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -320,15 +318,18 @@ hipError_t launch_segment(const DecodeArgs &d) {
 // covers the rows (8 at most; more rows take more workgroups).
 constexpr int64_t kMfmaMinRows = 2;
 
+bool use_mfma(int dtype, int64_t rows) { return dtype != kF32 && rows >= kMfmaMinRows; }
+int64_t valu_rows(int64_t rows) { return rows == 1 ? 1 : rows == 2 ? 2 : rows <= 4 ? 4 : 8; }
+
 template <typename T, int D>
 hipError_t launch_dim(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
     const int64_t rows = (a.H / d.Hkv) * a.N;
     hipError_t e;
-    if (!std::is_same<T, float>::value && rows >= kMfmaMinRows) e = launch_decode_segment_mfma(d);
-    else if (rows == 1) e = launch_segment<T, D, 1>(d);
-    else if (rows == 2) e = launch_segment<T, D, 2>(d);
-    else if (rows <= 4) e = launch_segment<T, D, 4>(d);
+    if (use_mfma(a.dtype, rows)) e = launch_decode_segment_mfma(d);
+    else if (valu_rows(rows) == 1) e = launch_segment<T, D, 1>(d);
+    else if (valu_rows(rows) == 2) e = launch_segment<T, D, 2>(d);
+    else if (valu_rows(rows) == 4) e = launch_segment<T, D, 4>(d);
     else e = launch_segment<T, D, 8>(d);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)),
@@ -348,6 +349,11 @@ hipError_t launch_typed(const DecodeArgs &d) {
 }
 
 }  // namespace
+
+int64_t decode_workgroups_per_split(int dtype, int64_t B, int64_t Hkv, int64_t rows) {
+    const int64_t per = use_mfma(dtype, rows) ? kDecodeMfmaRows : valu_rows(rows);
+    return B * Hkv * ((rows + per - 1) / per);
+}
 
 hipError_t launch_decode_splitkv(const DecodeArgs &d) {
     switch (d.a.dtype) {

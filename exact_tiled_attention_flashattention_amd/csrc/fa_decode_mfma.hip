@@ -57,7 +57,7 @@ template <> struct Mma<f16_t> {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 16;                 // query rows per workgroup
+constexpr int kRows = kDecodeMfmaRows;    // query rows per workgroup (16)
 constexpr int kBlk = 32;                  // keys per wave step
 constexpr uint32_t kOutOfRange = 0xC0000000u;   // past any head's K/V (< 2^31 bytes)
 
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
     constexpr int VL = kBlk * CPR / 64;     // 16-byte loads of K (and of V) per lane per block
     constexpr int WBYTES = kBlk * ROWB;     // one K (or V) block; later the wave's O^T partials
-    static_assert(KS >= 1 && VL >= 1 && kRows * D * 4 == WBYTES, "shape");
+    static_assert(kRows == 16 && KS >= 1 && VL >= 1 && kRows * D * 4 == WBYTES, "shape");
 
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[kWaves][WBYTES];
     __shared__ __attribute__((aligned(16))) unsigned char vbuf[kWaves][WBYTES];

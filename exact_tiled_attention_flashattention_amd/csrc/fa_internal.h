@@ -44,7 +44,12 @@ hipError_t launch_fwd_mfma_d128(const FwdArgs &a);   // fa_fwd_mfma_wide.hip
 
 // Split-KV decode: segment kernel then merge kernel, same stream.
 hipError_t launch_decode_splitkv(const DecodeArgs &a);
-// Matrix-core segment kernel (bf16/fp16), fa_decode_mfma.hip.
+// Matrix-core segment kernel (bf16/fp16), fa_decode_mfma.hip; it serves
+// kDecodeMfmaRows query rows per workgroup.
+constexpr int kDecodeMfmaRows = 16;
 hipError_t launch_decode_segment_mfma(const DecodeArgs &a);
+// Segment-kernel workgroups per split for `rows` = (Hq / Hkv) x N query rows
+// per key/value head (the same kernel choice as launch_decode_splitkv).
+int64_t decode_workgroups_per_split(int dtype, int64_t B, int64_t Hkv, int64_t rows);
 
 }  // namespace fa

@@ -120,9 +120,11 @@ size_t fa_decode_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t
  * (decode: N = 1) and long Nk; any N >= 1 gives the fa_fwd result.
  *
  *   q .. stream       as for fa_fwd (causal uses the same bottom-right mask).
- *   num_splits        segments per head, 1 .. 65536 (larger: FA_ERR_UNSUPPORTED);
- *                     it may exceed the key count, surplus segments are
- *                     then empty.  Also FA_ERR_UNSUPPORTED: B*H > 65535.
+ *   num_splits        segments per head, 1 .. 65536 (larger: FA_ERR_UNSUPPORTED;
+ *                     negative: FA_ERR_INVALID_ARG); it may exceed the key
+ *                     count, surplus segments are then empty.  0 selects
+ *                     fa_decode_splitkv_auto_splits(B, H, H, N, Nk, d,
+ *                     dtype) segments.  Also FA_ERR_UNSUPPORTED: B*H > 65535.
  *   workspace         device scratch of at least
  *                     fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits)
  *                     bytes, 16-byte aligned, owned by the caller; its
@@ -153,6 +155,8 @@ fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void 
  *             FA_ERR_INVALID_ARG; B * Hkv > 65535: FA_ERR_UNSUPPORTED).
  *   workspace at least fa_decode_splitkv_workspace_size(B, Hq, N, dv,
  *             num_splits) bytes (partials are kept per query head).
+ *   num_splits  as for fa_decode_splitkv; 0 selects
+ *             fa_decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dtype).
  *   all else  as for fa_decode_splitkv.
  */
 fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, void *o,
@@ -160,6 +164,27 @@ fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, v
                                   int64_t Nk, int64_t d, int64_t dv, int causal, float scale,
                                   fa_dtype_t dtype, int num_splits, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * fa_decode_splitkv_auto_splits -- the split count that num_splits = 0
+ * selects in the decode entry points for this shape (flash_lab.py section
+ * 4 chooses it with a time model; this library uses a rule measured on
+ * MI355X): the smallest power of two S for which the segment kernel has at
+ * least 512 workgroups, doubling S only while Nk >= 2 S * 256 (so that a
+ * segment keeps at least 256 keys), and S <= 256.  The workgroup count
+ * per split is B * Hkv * ceil(rows / r) with rows = (Hq / Hkv) * N and r the
+ * query rows per workgroup of the kernel the shape runs on (16 for bf16 and
+ * fp16 with rows >= 2; else the smallest of 1, 2, 4, 8 covering rows).
+ * Pure host logic: no HIP call.
+ *
+ *   B, Hq, Hkv, N, Nk, d, dtype   as for fa_decode_splitkv_gqa (d does not
+ *                                 change the current rule).
+ * Returns the split count (1 .. 256), or 0 if an argument is out of range
+ * (a size < 1, Hq % Hkv != 0, an unknown dtype, B * Hq or
+ * (Hq / Hkv) * N above 2^31 - 1).
+ */
+int fa_decode_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk,
+                                  int64_t d, fa_dtype_t dtype);
 
 /* fa_status_string -- a static, human-readable name of a status code. */
 const char *fa_status_string(fa_status_t status);

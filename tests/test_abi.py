@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import exact_tiled_attention_flashattention_amd as fa
 
@@ -25,7 +26,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_decode_splitkv", "fa_decode_splitkv_gqa",
+    assert _declared_functions() == ["fa_decode_splitkv", "fa_decode_splitkv_auto_splits",
+                                     "fa_decode_splitkv_gqa",
                                      "fa_decode_splitkv_workspace_size", "fa_fwd",
                                      "fa_status_string"]
 
@@ -107,7 +109,7 @@ def test_fwd_rejects(kw, expect):
 
 @no_gpu
 @pytest.mark.parametrize("kw,expect", [
-    (dict(ns=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ns=-1), fa.FA_ERR_INVALID_ARG),
     (dict(ns=-3), fa.FA_ERR_INVALID_ARG),
     (dict(q=None), fa.FA_ERR_INVALID_ARG),
     (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
@@ -118,6 +120,9 @@ def test_fwd_rejects(kw, expect):
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(ws=A + 4), fa.FA_ERR_WORKSPACE),
     (dict(wsb=1 * 1 * 4 * 1 * 65 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    # num_splits = 0 picks 16 splits for one head of 4096 keys: the workspace must hold 16
+    (dict(ns=0, Nk=4096, wsb=16 * 65 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(ns=0, Nk=4096, ws=None), fa.FA_ERR_WORKSPACE),
 ])
 def test_decode_rejects(kw, expect):
     assert _dec(**kw) == expect
@@ -136,7 +141,7 @@ def _gqa(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, N=1, Nk=64, d=64, dv=64, c
     (dict(Hq=0), fa.FA_ERR_INVALID_ARG),
     (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),     # not a multiple
     (dict(Hq=2, Hkv=4), fa.FA_ERR_INVALID_ARG),     # fewer query than key/value heads
-    (dict(ns=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ns=-1), fa.FA_ERR_INVALID_ARG),
     (dict(v=None), fa.FA_ERR_INVALID_ARG),
     (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
     (dict(B=256, Hq=512, Hkv=256), fa.FA_ERR_UNSUPPORTED),   # B * Hkv > 65535
@@ -146,6 +151,38 @@ def _gqa(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hkv=2, N=1, Nk=64, d=64, dv=64, c
 ])
 def test_decode_gqa_rejects(kw, expect):
     assert _gqa(**kw) == expect
+
+
+# (B, Hq, Hkv, N, Nk, d, dtype) -> split count, worked out by hand from the
+# documented rule: the smallest power of two S with (workgroups per split) * S
+# >= 512, doubled only while Nk >= 2 S * 256, at most 256.
+@pytest.mark.parametrize("shape,expect", [
+    ((8, 32, 32, 1, 32768, 128, torch.bfloat16), 2),     # 256 workgroups per split
+    ((8, 32, 8, 1, 32768, 128, torch.bfloat16), 8),      # 4 rows in one 16-row tile: 64 per split
+    ((1, 1, 1, 1, 64, 64, torch.bfloat16), 1),           # too few keys to split
+    ((1, 1, 1, 1, 511, 64, torch.bfloat16), 1),
+    ((1, 1, 1, 1, 512, 64, torch.bfloat16), 2),          # two segments of 256
+    ((1, 1, 1, 1, 4096, 64, torch.bfloat16), 16),        # stopped by the 256-key floor
+    ((1, 1, 1, 1, 1 << 20, 64, torch.bfloat16), 256),    # the cap
+    # 20 rows per key/value head: two 16-row tiles (bf16) or three 8-row groups (fp32)
+    ((12, 5, 1, 4, 1 << 20, 64, torch.bfloat16), 32),    # 24 workgroups per split
+    ((12, 5, 1, 4, 1 << 20, 64, torch.float32), 16),     # 36 workgroups per split
+    ((4, 8, 2, 1, 1 << 20, 128, torch.float16), 64),     # 4 rows, one tile: 8 per split
+])
+def test_auto_splits_rule(shape, expect):
+    assert fa.decode_splitkv_auto_splits(*shape) == expect
+
+
+def test_auto_splits_rejects():
+    f = fa.library().fa_decode_splitkv_auto_splits
+    assert f(1, 6, 4, 1, 100, 64, 2) == 0       # Hq not a multiple of Hkv
+    assert f(1, 4, 4, 0, 100, 64, 2) == 0       # N < 1
+    assert f(1, 4, 4, 1, 0, 64, 2) == 0         # Nk < 1
+    assert f(0, 4, 4, 1, 100, 64, 2) == 0       # B < 1
+    assert f(1, 4, 4, 1, 100, 64, 3) == 0       # unknown dtype
+    assert f(1 << 20, 1 << 12, 1, 1, 100, 64, 2) == 0   # B * Hq >= 2^31
+    with pytest.raises(ValueError):
+        fa.decode_splitkv_auto_splits(1, 6, 4, 1, 100, 64, torch.bfloat16)
 
 
 def test_binding_requires_gpu_tensors():

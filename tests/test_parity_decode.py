@@ -166,3 +166,33 @@ def test_gqa_b8_hq32_hkv8_nk32768_d128_sampled_heads():
     l_s = torch.stack([lse[b, h] for b, h in heads])
     compare(o_s, l_s, o_ref, l_ref, "bf16", "gqa full-size")
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+# ---- automatic split count (num_splits = 0) ---------------------------------
+
+@pytest.mark.parametrize("B,Hkv,G,N,Nk,d,dtype,causal", [
+    (2, 8, 1, 1, 5000, 128, "bf16", False),
+    (2, 4, 4, 1, 3000, 64, "f16", True),
+    (1, 4, 1, 2, 2000, 64, "f32", True),
+    (1, 2, 3, 3, 700, 32, "bf16", False),
+])
+def test_auto_splits_equals_explicit_count(B, Hkv, G, N, Nk, d, dtype, causal):
+    """num_splits = 0 runs exactly the split count the rule reports, and the
+    result is the oracle's."""
+    q, k, v, o, lse = _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, 0, seed=B + G + N)
+    S = fa.decode_splitkv_auto_splits(B, Hkv * G, Hkv, N, Nk, d, q.dtype)
+    assert S >= 1
+    o2, l2 = fa.decode_splitkv_gqa(q, k, v, causal=causal, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_auto_splits_plain_entry_point():
+    q, k, v = make_inputs(2, 4, 1, 6000, 128, 128, "bf16", 9)
+    o1, l1 = fa.decode_splitkv(q, k, v, num_splits=0)
+    S = fa.decode_splitkv_auto_splits(2, 4, 4, 1, 6000, 128, q.dtype)
+    o2, l2 = fa.decode_splitkv(q, k, v, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = oracle_on(q, k, v, False, default_scale(128))
+    compare(o1, l1, o_ref, l_ref, "bf16", "decode auto splits")
