@@ -64,6 +64,9 @@ class Oracle:
         lib.oracle_split_kv_decode.argtypes = [dp, dp, dp, L, L, L, L, L,
                                                ctypes.c_double, dp, dp]
         lib.oracle_split_kv_decode.restype = ctypes.c_int
+        lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, L, L, L,
+                                             ctypes.c_int, ctypes.c_double, ctypes.c_int]
+        lib.oracle_attention_bwd.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -96,6 +99,33 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle_attention failed with code {rc}")
         return (o, lse, p) if want_p else (o, lse)
+
+    def attention_bwd(self, q, k, v, dout, causal: bool = False, scale: float | None = None,
+                      nthreads: int | None = None):
+        """Backward of standard attention in FP64: the gradients (dq, dk, dv) of
+        sum(dout * O) with O = attention(q, k, v).  Shapes as :meth:`attention`,
+        dout like O."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        lead = q.shape[:-2]
+        N, d = q.shape[-2:]
+        Nk, dv = v.shape[-2:]
+        if (k.shape[:-2] != lead or v.shape[:-2] != lead or k.shape[-2:] != (Nk, d)
+                or dout.shape != lead + (N, dv)):
+            raise ValueError("shape mismatch between q, k, v, dout")
+        heads = int(np.prod(lead)) if lead else 1
+        if scale is None:
+            scale = 1.0 / np.sqrt(d)
+        dq = np.empty_like(q)
+        dk = np.empty_like(k)
+        dvv = np.empty_like(v)
+        if nthreads is None:
+            nthreads = max(1, len(os.sched_getaffinity(0)))
+        rc = self.lib.oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                                           _ptr(dk), _ptr(dvv), 1, heads, N, Nk, d, dv,
+                                           int(bool(causal)), float(scale), int(nthreads))
+        if rc != 0:
+            raise RuntimeError(f"oracle_attention_bwd failed with code {rc}")
+        return dq, dk, dvv
 
     def softmax_3pass(self, x):
         x = _f64(x)
@@ -196,3 +226,7 @@ def merge_states(a, b):
 
 def split_kv_decode(q, K, V, n_splits: int, scale: float | None = None):
     return default().split_kv_decode(q, K, V, n_splits, scale)
+
+
+def attention_bwd(*a, **kw):
+    return default().attention_bwd(*a, **kw)

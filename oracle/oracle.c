@@ -13,6 +13,7 @@
  *                                 merge_states
  *           §2 standard attention -- _causal_mask, standard_attention
  *           §4 flash-decoding  -- split_kv_decode
+ *           §5 backward        -- standard_attention_bwd
  *   [FF]  CS349E Lecture 11 "02_flash_forward.py", demo 1 (correctness): the
  *         flash forward computes exactly the standard result.
  *
@@ -374,4 +375,140 @@ int oracle_split_kv_decode(const double *q, const double *K, const double *V,
     free(seg_lse);
     free(s);
     return (int)used;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [FL] §5 standard attention backward, one head, from the materialised P    */
+/* of the forward definition above (a row with no visible key has P = 0):    */
+/*   D_i   = sum_c dO_ic O_ic                                                */
+/*   dV    = P^T dO                                                          */
+/*   dP    = dO V^T                                                          */
+/*   dS    = P o (dP - D)          (elementwise; D broadcast along a row)    */
+/*   dQ    = scale * dS K                                                    */
+/*   dK    = scale * dS^T Q                                                  */
+/* p [N, Nk], orow [dv] are caller scratch.                                  */
+/* ------------------------------------------------------------------------ */
+static void attention_bwd_head(const double *q, const double *k, const double *v,
+                               const double *dout, double *dq, double *dk,
+                               double *dvv, long N, long Nk, long d, long dv,
+                               int causal, double scale, double *p, double *o,
+                               double *lse, double *srow)
+{
+    attention_head(q, k, v, o, lse, p, N, Nk, d, dv, causal, scale, srow);
+    for (long x = 0; x < N * d; ++x)
+        dq[x] = 0.0;
+    for (long x = 0; x < Nk * d; ++x)
+        dk[x] = 0.0;
+    for (long x = 0; x < Nk * dv; ++x)
+        dvv[x] = 0.0;
+    for (long i = 0; i < N; ++i) {
+        const double *doi = dout + i * dv;
+        const double *oi = o + i * dv;
+        double Di = 0.0;
+        for (long c = 0; c < dv; ++c)
+            Di += doi[c] * oi[c];
+        for (long j = 0; j < Nk; ++j) {
+            double pij = p[i * Nk + j];
+            const double *vj = v + j * dv;
+            double *dvj = dvv + j * dv;
+            for (long c = 0; c < dv; ++c)
+                dvj[c] += pij * doi[c];                  /* dV = P^T dO */
+            double dpij = 0.0;
+            for (long c = 0; c < dv; ++c)
+                dpij += doi[c] * vj[c];                  /* dP = dO V^T */
+            double dsij = pij * (dpij - Di);             /* dS = P o (dP - D) */
+            const double *kj = k + j * d;
+            const double *qi = q + i * d;
+            double *dqi = dq + i * d;
+            double *dkj = dk + j * d;
+            for (long c = 0; c < d; ++c) {
+                dqi[c] += scale * dsij * kj[c];          /* dQ = scale dS K */
+                dkj[c] += scale * dsij * qi[c];          /* dK = scale dS^T Q */
+            }
+        }
+    }
+}
+
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *dq, *dk, *dv;
+    long H, N, Nk, d, dvd;
+    int causal;
+    double scale;
+    long head_begin, head_end;
+} bwd_job_t;
+
+static void *attention_bwd_worker(void *arg)
+{
+    bwd_job_t *jb = (bwd_job_t *)arg;
+    size_t np = (size_t)jb->N * (size_t)jb->Nk;
+    double *p = (double *)malloc(sizeof(double) * np);
+    double *o = (double *)malloc(sizeof(double) * (size_t)(jb->N * jb->dvd));
+    double *lse = (double *)malloc(sizeof(double) * (size_t)jb->N);
+    double *srow = (double *)malloc(sizeof(double) * (size_t)jb->Nk);
+    void *ret = NULL;
+    if (!p || !o || !lse || !srow) {
+        ret = (void *)1;
+    } else {
+        for (long h = jb->head_begin; h < jb->head_end; ++h)
+            attention_bwd_head(jb->q + h * jb->N * jb->d, jb->k + h * jb->Nk * jb->d,
+                               jb->v + h * jb->Nk * jb->dvd, jb->dout + h * jb->N * jb->dvd,
+                               jb->dq + h * jb->N * jb->d, jb->dk + h * jb->Nk * jb->d,
+                               jb->dv + h * jb->Nk * jb->dvd, jb->N, jb->Nk, jb->d, jb->dvd,
+                               jb->causal, jb->scale, p, o, lse, srow);
+    }
+    free(p);
+    free(o);
+    free(lse);
+    free(srow);
+    return ret;
+}
+
+/*
+ * Backward of standard attention over contiguous q[B,H,N,d], k[B,H,Nk,d],
+ * v[B,H,Nk,dv] and the output gradient dout[B,H,N,dv]: writes dq[B,H,N,d],
+ * dk[B,H,Nk,d], dv[B,H,Nk,dv].  Threads over heads as oracle_attention; the
+ * result does not depend on the thread count.  Returns 0, -1 on bad
+ * arguments, -2 if a thread or buffer could not be created.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk, double *dv,
+                         long B, long H, long N, long Nk, long d, long dvd,
+                         int causal, double scale, int nthreads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 1 || H < 1 || N < 1 ||
+        Nk < 1 || d < 1 || dvd < 1)
+        return -1;
+    long heads = B * H;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > heads)
+        nthreads = (int)heads;
+    bwd_job_t *jobs = (bwd_job_t *)calloc((size_t)nthreads, sizeof(bwd_job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -2;
+    }
+    int rc = 0;
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (bwd_job_t){q, k, v, dout, dq, dk, dv, H, N, Nk, d, dvd, causal, scale,
+                              heads * t / nthreads, heads * (t + 1) / nthreads};
+        if (pthread_create(&th[t], NULL, attention_bwd_worker, &jobs[t]) != 0) {
+            rc = -2;
+            break;
+        }
+        ++started;
+    }
+    for (int t = 0; t < started; ++t) {
+        void *ret = NULL;
+        pthread_join(th[t], &ret);
+        if (ret)
+            rc = -2;
+    }
+    free(jobs);
+    free(th);
+    return rc;
 }

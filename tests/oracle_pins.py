@@ -11,7 +11,8 @@ Run as ``python -m tests.oracle_pins <liboracle.so>`` to print the names of the
 failing pins as JSON (used by the mutant test, one subprocess per build).
 
 Citations name the page and section: [FL] = CS349E Lecture 11 shared module
-flash_lab.py; [XS] = xserv design doc "04-transformer-kernels", test plan.
+flash_lab.py (section 5 is the backward); [XS] = xserv design doc
+"04-transformer-kernels", test plan.
 """
 from __future__ import annotations
 
@@ -400,6 +401,138 @@ def pin_split_kv_decode(orc):
         assert used == min(ns, 1000), (ns, used)
         assert np.abs(o - ot).max() < 1e-13, f"split {ns} O"
         assert np.abs(lse - lt).max() < 1e-13, f"split {ns} LSE"
+
+
+# --------------------------------------------------------------------------
+# pins of the backward ([FL] section 5, standard_attention_bwd)
+# --------------------------------------------------------------------------
+def _loss(orc, q, k, v, dout, causal, scale):
+    """sum(dout * O): the scalar whose gradient the backward returns."""
+    o, _ = orc.attention(q, k, v, causal=causal, scale=scale)
+    return float(np.sum(dout * o))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every entry of dq, dk, dv against a central difference of
+    sum(dout * O) through the (separately pinned) forward, as the pages'
+    self-test does for one entry (step 1e-6, agreement to 1e-7)."""
+    rng = _rng(41)
+    eps = 1e-6
+    for (N, Nk, d, dv, causal) in ((5, 7, 3, 2, False), (4, 4, 3, 3, True), (6, 4, 2, 3, True)):
+        q = rng.standard_normal((N, d))
+        k = rng.standard_normal((Nk, d))
+        v = rng.standard_normal((Nk, dv))
+        dout = rng.standard_normal((N, dv))
+        grads = orc.attention_bwd(q, k, v, dout, causal=causal, scale=0.7)
+        for which, x in enumerate((q, k, v)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                args = [q, k, v]
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args[which] = xp
+                fp = _loss(orc, *args, dout, causal, 0.7)
+                args[which] = xm
+                fm = _loss(orc, *args, dout, causal, 0.7)
+                num[idx] = (fp - fm) / (2 * eps)
+            _close(grads[which], num, 1e-7, f"finite differences d{'qkv'[which]} {N}x{Nk} causal={causal}")
+
+
+def pin_bwd_single_key(orc):
+    """Nk = 1: O_i = v0 whatever q and k are, so dq = dk = 0 and
+    dv0 = sum_i dout_i."""
+    rng = _rng(42)
+    q = rng.standard_normal((5, 4))
+    k = rng.standard_normal((1, 4))
+    v = rng.standard_normal((1, 3))
+    dout = rng.standard_normal((5, 3))
+    dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal=False, scale=0.5)
+    _close(dq, np.zeros_like(q), 1e-15, "Nk=1 dq")
+    _close(dk, np.zeros_like(k), 1e-15, "Nk=1 dk")
+    _close(dv, dout.sum(axis=0, keepdims=True), 1e-14, "Nk=1 dv")
+
+
+def pin_bwd_scale_zero(orc):
+    """scale = 0: the weights are 1/#visible whatever q and k are, so
+    dq = dk = 0 and dv_j = sum over the rows i that see key j of
+    dout_i / #visible_i."""
+    rng = _rng(43)
+    for (N, Nk, causal) in ((5, 5, False), (5, 5, True), (3, 6, True), (6, 3, True)):
+        q = rng.standard_normal((N, 4))
+        k = rng.standard_normal((Nk, 4))
+        v = rng.standard_normal((Nk, 2))
+        dout = rng.standard_normal((N, 2))
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal=causal, scale=0.0)
+        _close(dq, np.zeros_like(q), 0.0, "scale=0 dq")
+        _close(dk, np.zeros_like(k), 0.0, "scale=0 dk")
+        cnt = _visible_count(N, Nk, causal)
+        want = np.zeros((Nk, 2))
+        for i in range(N):
+            for j in range(Nk):
+                if (not causal or j <= Nk - N + i) and cnt[i] > 0:
+                    want[j] += dout[i] / cnt[i]
+        _close(dv, want, 1e-14, f"scale=0 dv {N}x{Nk} causal={causal}")
+
+
+def pin_bwd_invariants(orc):
+    """Facts of the gradient that hold at any size:
+    * each row of dS sums to 0 (softmax is invariant to a shift of a row's
+      scores), so sum_j dk_j = 0;
+    * each row of P sums to 1 (0 for a row that sees no key), so
+      sum_j dv_j = sum of dout over the rows that see some key;
+    * scaling q by t scales the scores like scaling k by t, so
+      sum(q * dq) = sum(k * dk)."""
+    rng = _rng(44)
+    for (N, Nk, causal) in ((9, 13, False), (9, 13, True), (12, 7, True)):
+        q = rng.standard_normal((N, 6))
+        k = rng.standard_normal((Nk, 6))
+        v = rng.standard_normal((Nk, 5))
+        dout = rng.standard_normal((N, 5))
+        dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal=causal, scale=0.4)
+        _close(dk.sum(axis=0), np.zeros(6), 1e-13, "sum of dk")
+        seen = _visible_count(N, Nk, causal) > 0
+        _close(dv.sum(axis=0), dout[seen].sum(axis=0), 1e-13, "sum of dv")
+        _close(np.sum(q * dq), np.sum(k * dk), 1e-12, "q.dq = k.dk")
+
+
+def pin_bwd_torch_autograd(orc):
+    """torch float64 autograd through softmax with an explicit bottom-right
+    mask (a different code base), on shapes where every row sees a key."""
+    import torch
+    rng = _rng(45)
+    for (N, Nk, d, dv, causal) in ((17, 23, 8, 5, False), (17, 23, 8, 5, True), (16, 16, 4, 4, True)):
+        q = rng.standard_normal((N, d))
+        k = rng.standard_normal((Nk, d))
+        v = rng.standard_normal((Nk, dv))
+        dout = rng.standard_normal((N, dv))
+        qt, kt, vt = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        s = (qt @ kt.transpose(0, 1)) * 0.35
+        if causal:
+            allowed = torch.arange(Nk)[None, :] <= (Nk - N + torch.arange(N))[:, None]
+            s = s.masked_fill(~allowed, float("-inf"))
+        o = torch.softmax(s, dim=-1) @ vt
+        o.backward(torch.from_numpy(dout))
+        dq, dk, dvv = orc.attention_bwd(q, k, v, dout, causal=causal, scale=0.35)
+        _close(dq, qt.grad.numpy(), 1e-12, "autograd dq")
+        _close(dk, kt.grad.numpy(), 1e-12, "autograd dk")
+        _close(dvv, vt.grad.numpy(), 1e-12, "autograd dv")
+
+
+def pin_bwd_heads_independent(orc):
+    """Batched heads give the per-head results (the head strides are right)."""
+    rng = _rng(46)
+    q = rng.standard_normal((2, 3, 5, 4))
+    k = rng.standard_normal((2, 3, 6, 4))
+    v = rng.standard_normal((2, 3, 6, 3))
+    dout = rng.standard_normal((2, 3, 5, 3))
+    dq, dk, dv = orc.attention_bwd(q, k, v, dout, causal=True, scale=0.5)
+    for b in range(2):
+        for h in range(3):
+            g = orc.attention_bwd(q[b, h], k[b, h], v[b, h], dout[b, h], causal=True, scale=0.5)
+            _close(dq[b, h], g[0], 0.0, "head dq")
+            _close(dk[b, h], g[1], 0.0, "head dk")
+            _close(dv[b, h], g[2], 0.0, "head dv")
 
 
 PINS = [v for k, v in list(globals().items()) if k.startswith("pin_") and callable(v)]

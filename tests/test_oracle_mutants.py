@@ -44,6 +44,14 @@ MUTANTS = {
                                 "acc += exp(seg_lse[u * R + r] - big)"),
     "split_segment_unnormalised": ("os[c] /= lr;", "os[c] /= 1.0;"),
     "split_last_bound": ("long b = (sp + 1 == n_splits) ? S :", "long b = (sp + 1 == n_splits) ? S - 1 :"),
+    "bwd_D_dropped": ("double dsij = pij * (dpij - Di);", "double dsij = pij * dpij;"),
+    "bwd_dS_sign": ("double dsij = pij * (dpij - Di);", "double dsij = pij * (Di - dpij);"),
+    "bwd_D_from_v": ("Di += doi[c] * oi[c];", "Di += doi[c] * v[c];"),
+    "bwd_dP_from_o": ("dpij += doi[c] * vj[c];", "dpij += doi[c] * oi[c];"),
+    "bwd_dq_unscaled": ("dqi[c] += scale * dsij * kj[c];", "dqi[c] += dsij * kj[c];"),
+    "bwd_dk_from_k": ("dkj[c] += scale * dsij * qi[c];", "dkj[c] += scale * dsij * kj[c];"),
+    "bwd_dv_row_index": ("double *dvj = dvv + j * dv;", "double *dvj = dvv + (i % Nk) * dv;"),
+    "bwd_dv_from_v": ("dvj[c] += pij * doi[c];", "dvj[c] += pij * vj[c];"),
 }
 
 
