@@ -29,7 +29,8 @@ MUTANTS = {
     "no_normalisation": ("double pij = srow[j] / l;", "double pij = srow[j];"),
     "exp_sign": ("srow[j] = exp(srow[j] - m);", "srow[j] = exp(m - srow[j]);"),
     "k_transposed": ("acc += qi[c] * kj[c];", "acc += qi[c] * k[c * Nk + j];"),
-    "v_wrong_stride": ("const double *vj = v + j * dv;", "const double *vj = v + j;"),
+    "v_wrong_stride": ("const double *vj = v + j * dv;\n            for (long c = 0; c < dv; ++c)\n                oi[c]",
+                       "const double *vj = v + j;\n            for (long c = 0; c < dv; ++c)\n                oi[c]"),
     "empty_row_nan": ("if (m == -INFINITY) {                    /* R1",
                       "if (0) {                    /* R1"),
     "online_no_carry": ("l = l * carry + add;", "l = l + add;"),
