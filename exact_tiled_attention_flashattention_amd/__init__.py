@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "fwd", "decode_splitkv", "decode_splitkv_gqa", "decode_splitkv_workspace_size",
-    "decode_splitkv_auto_splits", "status_string",
+    "decode_splitkv_auto_splits", "bwd", "bwd_workspace_size", "status_string",
     "FAError", "library", "LIBRARY_PATH", "FA_OK", "FA_ERR_INVALID_ARG",
     "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
 ]
@@ -64,6 +64,11 @@ def library() -> ctypes.CDLL:
     lib.fa_decode_splitkv_gqa.restype = c_int
     lib.fa_decode_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, i64, i64, c_int]
     lib.fa_decode_splitkv_auto_splits.restype = c_int
+    lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                           c_int, ctypes.c_float, c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd.restype = c_int
     lib.fa_status_string.argtypes = [c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -129,6 +134,48 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
     return out, lse
+
+
+def bwd_workspace_size(B: int, H: int, N: int) -> int:
+    return int(library().fa_bwd_workspace_size(B, H, N))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, causal: bool = False, scale: float | None = None,
+        workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
+        dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+        stream: torch.cuda.Stream | None = None):
+    """Attention backward through ``fa_bwd``.
+
+    ``o`` and ``lse`` are :func:`fwd`'s outputs for the same q, k, v, causal
+    and scale; ``dout`` is the gradient of the loss with respect to ``o``.
+    Returns ``(dq, dk, dv)`` in the input dtype.
+    """
+    B, H, N, Nk, d, dvd = _check_qkv(q, k, v)
+    for name, t, shape, dtype in (("o", o, (B, H, N, dvd), q.dtype),
+                                  ("dout", dout, (B, H, N, dvd), q.dtype),
+                                  ("lse", lse, (B, H, N), torch.float32)):
+        if (not isinstance(t, torch.Tensor) or tuple(t.shape) != shape or t.dtype != dtype
+                or t.device != q.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape} "
+                             f"on {q.device}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_size(B, H, N), 16), dtype=torch.uint8,
+                                device=q.device)
+    st = library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          B, H, N, Nk, d, dvd, int(bool(causal)), float(scale),
+                          _DTYPE_CODE[q.dtype], workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(),
+                          _stream_handle(q.device, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def decode_splitkv_workspace_size(B: int, H: int, N: int, dv: int, num_splits: int) -> int:

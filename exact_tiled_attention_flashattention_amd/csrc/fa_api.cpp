@@ -201,6 +201,41 @@ fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, v
                        num_splits, workspace, workspace_bytes, stream);
 }
 
+size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N) {
+    if (B < 1 || H < 1 || N < 1) return 0;
+    int64_t x;
+    if (!mul_ok(B, H, &x) || !mul_ok(x, N, &x) || !mul_ok(x, 4, &x)) return 0;
+    if ((uint64_t)x > (uint64_t)std::numeric_limits<size_t>::max()) return 0;
+    return static_cast<size_t>(x);
+}
+
+fa_status_t fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
+                   int64_t N, int64_t Nk, int64_t d, int64_t dv_dim, int causal, float scale,
+                   fa_dtype_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    // o and lse are inputs here; check_common treats them like the forward's outputs.
+    fa_status_t st = check_common(q, k, v, o, lse, B, H, N, Nk, d, dv_dim, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return FA_ERR_INVALID_ARG;
+    if (B * H * ((N > Nk ? N : Nk) + 3) / 4 > kMaxI32) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_bwd_workspace_size(B, H, N);
+    if (need == 0) return FA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    fa::BwdArgs b;
+    b.a = make_args(q, k, v, const_cast<void *>(o), const_cast<float *>(lse), B, H, N, Nk, d,
+                    dv_dim, causal, scale, dtype, stream);
+    b.dout = dout;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.Dsum = static_cast<float *>(workspace);
+    (void)hipGetLastError();
+    hipError_t e = fa::launch_bwd(b);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int fa_decode_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk,
                                   int64_t d, fa_dtype_t dtype) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || Nk < 1 || d < 1 ||

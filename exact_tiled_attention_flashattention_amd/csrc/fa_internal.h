@@ -34,6 +34,15 @@ struct DecodeArgs {
     float *ws_lse;        // [B, H, num_splits, N]
 };
 
+struct BwdArgs {
+    FwdArgs a;            // q, k, v, o (forward output), lse (forward output), sizes
+    const void *dout;     // [B, H, N, dv]
+    void *dq;             // [B, H, N, d]   (written)
+    void *dk;             // [B, H, Nk, d]  (written)
+    void *dv;             // [B, H, Nk, dv] (written)
+    float *Dsum;          // workspace [B, H, N]: D_i = sum_c dO_ic O_ic
+};
+
 // Row-parallel VALU forward: any dtype, d == dv in {32, 64, 128}.
 hipError_t launch_fwd_rowwise(const FwdArgs &a);
 
@@ -51,5 +60,11 @@ hipError_t launch_decode_segment_mfma(const DecodeArgs &a);
 // Segment-kernel workgroups per split for `rows` = (Hq / Hkv) x N query rows
 // per key/value head (the same kernel choice as launch_decode_splitkv).
 int64_t decode_workgroups_per_split(int dtype, int64_t B, int64_t Hkv, int64_t rows);
+
+// Backward (fa_bwd.hip): row dots, then dQ and (dK, dV); the matrix-core
+// kernels (fa_bwd_mfma.hip) take bf16/fp16 with d == dv in {64, 128}.
+hipError_t launch_bwd(const BwdArgs &b);
+bool bwd_mfma_supported(int dtype, int64_t d, int64_t dv);
+hipError_t launch_bwd_mfma(const BwdArgs &b);
 
 }  // namespace fa

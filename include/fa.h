@@ -186,6 +186,45 @@ fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, v
 int fa_decode_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk,
                                   int64_t d, fa_dtype_t dtype);
 
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: one
+ * float32 per query row, B * H * N * 4.  Returns 0 if an argument is < 1 or
+ * the size overflows.
+ */
+size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
+
+/*
+ * fa_bwd -- gradients of exact attention (the FlashAttention-2 backward of
+ * flash_lab.py section 5, flash_bwd): given the forward's inputs, its outputs
+ * o and lse (as fa_fwd writes them) and the output gradient dout, writes
+ *     dq = dL/dq, dk = dL/dk, dv = dL/dv   for L = sum(dout * O),
+ * i.e. with P = exp(S - LSE) recomputed from q, k and lse (never stored),
+ *     D_i = sum_c dout_ic o_ic,  dv = P^T dout,  dP = dout v^T,
+ *     dS = P * (dP - D),  dq = scale dS k,  dk = scale dS^T q,
+ * the gradients section 5's standard_attention_bwd defines.  Rows that see
+ * no key (lse = -inf) contribute nothing; keys no row sees get dk = dv = 0.
+ *
+ *   q, k, v, causal, scale, dtype, sizes   as for fa_fwd (the same call).
+ *   o, lse     fa_fwd's outputs for these inputs (read; same layout).
+ *   dout       [B, H, N, dv] element type `dtype`, 16-byte aligned (read).
+ *   dq, dk, dv [B, H, N, d], [B, H, Nk, d], [B, H, Nk, dv], element type
+ *              `dtype`, 16-byte aligned (written, round-to-nearest-even).
+ *   workspace  device scratch of at least fa_bwd_workspace_size(B, H, N)
+ *              bytes, 16-byte aligned, owned by the caller (the row dots D);
+ *              contents on entry ignored, on exit undefined.
+ * Arithmetic: products accumulated in float32; for bf16/fp16 with d = dv in
+ * {64, 128} the probabilities and dS are rounded to `dtype` before the
+ * products that use them (matrix cores), other shapes and fp32 stay in
+ * float32 throughout.  Deterministic: every output element is written by
+ * one workgroup.  Returns FA_OK, FA_ERR_INVALID_ARG (as fa_fwd, plus null or
+ * misaligned dout/dq/dk/dv), FA_ERR_UNSUPPORTED (as fa_fwd), FA_ERR_WORKSPACE
+ * or FA_ERR_LAUNCH.
+ */
+fa_status_t fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
+                   int64_t N, int64_t Nk, int64_t d, int64_t dv_dim, int causal, float scale,
+                   fa_dtype_t dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 /* fa_status_string -- a static, human-readable name of a status code. */
 const char *fa_status_string(fa_status_t status);
 

@@ -5,6 +5,13 @@ Tolerances (max absolute error against the FP64 oracle):
   fp32 inputs:       O <= 2e-5, LSE <= 2e-5
   bf16/fp16 inputs:  O <= 2e-2, LSE <= 1e-2
 LSE = -inf (a row that sees no key) must match exactly, with O = 0 there.
+
+Gradients (dq, dk, dv of the backward) use the same per-dtype bars on O,
+relative to the gradient's own scale: max|g - g_ref| <= tol * max(1,
+max|g_ref|).  O is a convex combination of V rows (unit scale); a gradient
+is a sum over up to N rows or Nk keys and grows with them, and its bf16
+rounding error (and that of the rounded P and dS the matrix cores use)
+grows in proportion.
 """
 from __future__ import annotations
 
@@ -51,6 +58,35 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what: str, tol=None):
     assert err_o <= tol_o, f"{what}: O error {err_o:.3e} > {tol_o:.0e}"
     assert err_l <= tol_l, f"{what}: LSE error {err_l:.3e} > {tol_l:.0e}"
     return err_o, err_l
+
+
+GRAD_TOL = {"f32": 2e-5, "bf16": 2e-2, "f16": 2e-2}
+
+
+def compare_grads(got, ref, dtype: str, what: str):
+    """Assert (dq, dk, dv) match the oracle's within GRAD_TOL (relative to
+    max(1, max|ref|) per tensor); returns the three errors."""
+    errs = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = si.as_f64(g)
+        assert g.shape == r.shape, (what, name, g.shape, r.shape)
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        err = float(np.max(np.abs(g - r))) if g.size else 0.0
+        bound = GRAD_TOL[dtype] * max(1.0, float(np.max(np.abs(r))) if r.size else 0.0)
+        log(f"  {what}: max|d{name}|={err:.3e} (bar {bound:.2e})")
+        assert err <= bound, f"{what}: {name} error {err:.3e} > {bound:.2e}"
+        errs.append(err)
+    return errs
+
+
+def oracle_bwd_on(q, k, v, dout, causal, scale, heads=None):
+    """Oracle gradients on the GPU tensors' values; ``heads`` = list of (b, h)."""
+    f = lambda t: si.as_f64(t)
+    if heads is None:
+        return oracle.attention_bwd(f(q), f(k), f(v), f(dout), causal=causal, scale=scale)
+    parts = [oracle.attention_bwd(f(q[b, h]), f(k[b, h]), f(v[b, h]), f(dout[b, h]),
+                                  causal=causal, scale=scale) for (b, h) in heads]
+    return tuple(np.stack([p[i] for p in parts]) for i in range(3))
 
 
 def oracle_on(q, k, v, causal, scale, heads=None):

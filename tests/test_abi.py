@@ -26,7 +26,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_decode_splitkv", "fa_decode_splitkv_auto_splits",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode_splitkv",
+                                     "fa_decode_splitkv_auto_splits",
                                      "fa_decode_splitkv_gqa",
                                      "fa_decode_splitkv_workspace_size", "fa_fwd",
                                      "fa_status_string"]
@@ -153,6 +154,44 @@ def test_decode_gqa_rejects(kw, expect):
     assert _gqa(**kw) == expect
 
 
+def _bwd(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, B=1, H=1, N=4, Nk=4, d=64,
+         dvd=64, causal=0, scale=0.125, dtype=2, ws=A, wsb=1 << 20):
+    return fa.library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, Nk, d, dvd, causal,
+                               scale, dtype, ws, wsb, None)
+
+
+def test_bwd_workspace_size():
+    assert fa.bwd_workspace_size(2, 3, 5) == 2 * 3 * 5 * 4
+    assert fa.bwd_workspace_size(0, 3, 5) == 0
+    assert fa.bwd_workspace_size(1 << 40, 1 << 20, 1 << 20) == 0
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=A + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=A + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=A + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=48, dvd=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64, dvd=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 4), fa.FA_ERR_WORKSPACE),
+    (dict(B=2, H=3, N=5, wsb=2 * 3 * 5 * 4 - 1), fa.FA_ERR_WORKSPACE),
+])
+def test_bwd_rejects(kw, expect):
+    assert _bwd(**kw) == expect
+
+
 # (B, Hq, Hkv, N, Nk, d, dtype) -> split count, worked out by hand from the
 # documented rule: the smallest power of two S with (workgroups per split) * S
 # >= 512, doubled only while Nk >= 2 S * 256, at most 256.
@@ -194,3 +233,5 @@ def test_binding_requires_gpu_tensors():
         fa.decode_splitkv(x, x, x)
     with pytest.raises(ValueError):
         fa.decode_splitkv_gqa(x, x, x)
+    with pytest.raises(ValueError):
+        fa.bwd(x, x, x, x, torch.zeros(1, 1, 4), x)

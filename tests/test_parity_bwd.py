@@ -1,0 +1,82 @@
+"""fa_bwd (through the C ABI) against the FP64 oracle's backward on the GPU.
+
+The forward outputs o and lse that fa_bwd consumes come from fa_fwd on the
+same inputs, as a training step would pass them."""
+import pytest
+import torch
+
+import exact_tiled_attention_flashattention_amd as fa
+import synth_inputs as si
+from tests.parity import compare_grads, default_scale, log, make_inputs, oracle_bwd_on
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, N, Nk, d, dtype, seed, std=1.0):
+    q, k, v = make_inputs(B, H, N, Nk, d, d, dtype, seed, std)
+    dout, _, _ = make_inputs(B, H, N, 1, d, d, dtype, seed + 500)
+    return q, k, v, dout
+
+
+def _run(B, H, N, Nk, d, dtype, causal, seed=0, std=1.0, scale=None):
+    q, k, v, dout = _inputs(B, H, N, Nk, d, dtype, seed, std)
+    scale = default_scale(d) if scale is None else scale
+    log(f"fa_bwd dtype={dtype} B={B} H={H} N={N} Nk={Nk} d={d} causal={causal} seed={seed}")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    grads = fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle_bwd_on(q, k, v, dout, causal, scale)
+    compare_grads(grads, ref, dtype, f"bwd {dtype} {B}x{H}x{N}x{Nk}x{d} causal={causal}")
+    return grads
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("N,Nk", [(77, 513), (300, 300), (129, 1), (1, 1000), (40, 17)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged(dtype, d, N, Nk, causal):
+    _run(1, 2, N, Nk, d, dtype, causal, seed=N + Nk + d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_several_blocks(dtype, d, causal):
+    # several query and key blocks of every kernel, with ragged ends
+    _run(2, 3, 700, 650, d, dtype, causal, seed=d + int(causal))
+
+
+def test_scale_zero():
+    # uniform weights: dq = dk = 0
+    dq, dk, dv = _run(1, 2, 64, 96, 64, "bf16", True, seed=3, scale=0.0)
+    assert torch.count_nonzero(dq).item() == 0 and torch.count_nonzero(dk).item() == 0
+
+
+def test_deterministic():
+    q, k, v, dout = _inputs(2, 2, 333, 444, 64, "bf16", 7)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd(q, k, v, o, lse, dout, causal=True)
+    g2 = fa.bwd(q, k, v, o, lse, dout, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+def test_prefill_b64_h16_n1024_d64_sampled_heads():
+    """The backward at the B64 x H16 x 1024 causal prefill size, in the launch
+    configuration the benchmark times; the oracle checks two whole heads."""
+    w = si.WORKLOADS["prefill_b64_h16_n1024_d64"]
+    s = w.shapes[0]
+    log(f"fa_bwd full-size {w.name}")
+    q, k, v = si.device_qkv(s, w.seed, w.dtype, "cuda", w.std)
+    dout, _, _ = si.device_qkv(si.Shape(s.B, s.H, s.N, 1, s.dv, s.dv), w.seed + 100, w.dtype,
+                               "cuda", 1.0)
+    scale = default_scale(s.d)
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dout, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (s.B - 1, s.H - 1)]
+    ref = oracle_bwd_on(q, k, v, dout, True, scale, heads=heads)
+    got = tuple(torch.stack([g[b, h] for b, h in heads]) for g in (dq, dk, dv))
+    compare_grads(got, ref, "bf16", "bwd full-size")
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all().item()
