@@ -360,6 +360,57 @@ def split_sweep(args, torch, fa) -> int:
     return 0
 
 
+def bench_bwd(args, torch, fa, si, dev) -> int:
+    """Backward (fa_bwd) at the B64 x H16 x 1024 causal prefill size: one step
+    is one fa_bwd call (row dots, dK/dV kernel, dQ kernel) on the forward's o
+    and lse.  Credited FLOPs are 2.5 times the forward's (five matrix
+    products per tile instead of two; the lecture's count), causal-halved."""
+    w = si.WORKLOADS[PREFILL]
+    s = w.shapes[0]
+    q, k, v = si.device_qkv(s, w.seed, w.dtype, dev, w.std)
+    dout, _, _ = si.device_qkv(si.Shape(s.B, s.H, s.N, 1, s.dv, s.dv), w.seed + 100, w.dtype,
+                               dev, 1.0)
+    scale = 1.0 / math.sqrt(s.d)
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_size(s.B, s.H, s.N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        fa.bwd(q, k, v, o, lse, dout, causal=True, scale=scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i].record(stream)
+        call()
+    ev[args.steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    avg_s = sum(ms) / len(ms) / 1e3
+    flop = 2.5 * 4.0 * s.N * s.Nk * s.d * s.B * s.H / 2
+    tf = flop / avg_s / 1e12
+    print(json.dumps({
+        "metric": "attn bwd TFLOP/s (% bf16 MFMA peak)", "value": round(tf, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded torch Philox draws on the GPU)",
+        "config": {"workload": PREFILL + " (fa_bwd)", "B": s.B, "H": s.H, "N": s.N, "Nk": s.Nk,
+                   "d": s.d, "causal": True},
+        "roofline": {"kernel": "bwd_dkdv_mfma_kernel + bwd_dq_mfma_kernel (+ bwd_dot_kernel)",
+                     "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(avg_s * 1e6, 2), "min_launch_us": round(min(ms) * 1e3, 2),
+                     "credited_flop_per_launch": flop},
+    }))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,9 +421,10 @@ def main() -> int:
                     help="prefill heads the CPU oracle is timed on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="add one plain 1 GiB device copy per step (for counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "gqa"],
+    ap.add_argument("--only", choices=["prefill", "decode", "gqa", "bwd"],
                     help="profile one entry point alone (the JSON line then omits the other); "
-                         "'gqa' times the grouped-query decode (not part of the default line)")
+                         "'gqa' times the grouped-query decode, 'bwd' the backward (neither is "
+                         "part of the default line)")
     ap.add_argument("--split-sweep", action="store_true",
                     help="time decode at every candidate split count over a set of shapes "
                          "and write the table under profiles/")
@@ -404,6 +456,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.only == "gqa":
         return bench_gqa(args, torch, fa, si, dev)
+    if args.only == "bwd":
+        return bench_bwd(args, torch, fa, si, dev)
     if args.split_sweep:
         return split_sweep(args, torch, fa)
     wp = si.WORKLOADS[PREFILL]

@@ -25,21 +25,27 @@
 namespace fa {
 namespace {
 
-// D_i = sum_c dO_ic O_ic in fp32.  16 lanes per row, 4 rows per wave.
-template <typename T>
+// D_i = sum_c dO_ic O_ic in fp32.  A row is read as 16-byte pieces by
+// LPR = DV * sizeof(T) / 16 consecutive lanes; 256 / LPR rows per workgroup.
+template <typename T, int DV>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const T *__restrict__ o,
                                                       const T *__restrict__ dout,
-                                                      float *__restrict__ D, int64_t rows,
-                                                      int dv) {
-    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;
-    const int t = threadIdx.x % 16;
+                                                      float *__restrict__ D, int64_t rows) {
+    constexpr int EPL = 16 / (int)sizeof(T);
+    constexpr int LPR = DV / EPL;
+    static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row split");
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int t = threadIdx.x % LPR;
     float acc = 0.f;
     if (row < rows) {
-        const T *orow = o + row * dv;
-        const T *drow = dout + row * dv;
-        for (int c = t; c < dv; c += 16) acc = fmaf(to_f32(orow[c]), to_f32(drow[c]), acc);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(o + row * DV + t * EPL);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + row * DV + t * EPL);
+        const T *ea = reinterpret_cast<const T *>(&a);
+        const T *eb = reinterpret_cast<const T *>(&b);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(to_f32(ea[e]), to_f32(eb[e]), acc);
     }
-    acc = group_sum<16>(acc);
+    acc = group_sum<LPR>(acc);
     if (row < rows && t == 0) D[row] = acc;
 }
 
@@ -199,14 +205,22 @@ hipError_t launch_rowwise(const BwdArgs &b) {
     return hipGetLastError();
 }
 
+template <typename T, int DV>
+hipError_t launch_dot(const BwdArgs &b) {
+    const FwdArgs &a = b.a;
+    const int64_t rows = a.B * a.H * a.N;
+    constexpr int rpb = 256 / (DV * (int)sizeof(T) / 16);   // rows per workgroup
+    hipLaunchKernelGGL((bwd_dot_kernel<T, DV>), dim3((unsigned)((rows + rpb - 1) / rpb)),
+                       dim3(256), 0, a.stream, static_cast<const T *>(a.o),
+                       static_cast<const T *>(b.dout), b.Dsum, rows);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_typed(const BwdArgs &b) {
     const FwdArgs &a = b.a;
-    const int64_t rows = a.B * a.H * a.N;
-    hipLaunchKernelGGL((bwd_dot_kernel<T>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                       a.stream, static_cast<const T *>(a.o), static_cast<const T *>(b.dout),
-                       b.Dsum, rows, (int)a.dv);
-    hipError_t e = hipGetLastError();
+    hipError_t e = a.dv == 32 ? launch_dot<T, 32>(b) : a.dv == 64 ? launch_dot<T, 64>(b)
+                                                                  : launch_dot<T, 128>(b);
     if (e != hipSuccess) return e;
     if (bwd_mfma_supported(a.dtype, a.d, a.dv)) return launch_bwd_mfma(b);
     switch (a.d) {

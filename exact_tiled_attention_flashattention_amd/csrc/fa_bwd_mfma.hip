@@ -1,11 +1,545 @@
-// fa_bwd_mfma.hip -- attention backward on the CDNA4 matrix cores.
+// fa_bwd_mfma.hip -- attention backward on the CDNA4 matrix cores
+// (bf16/fp16 inputs, d == dv in {64, 128}, fp32 accumulation).
+//
+// Method: CS349E Lecture 11 "flash_lab.py", section 5 (flash_bwd, the
+// FlashAttention-2 backward).  The probabilities are recomputed from Q, K
+// and the forward's LSE, P = exp(S - LSE) (here exp2 of S scale log2(e) -
+// LSE log2(e)); with D_i = rowsum(dO o O) (the row-dot kernel of fa_bwd.hip):
+//     dV += P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+//     dK += dS^T Q (times scale),  dQ += dS K (times scale).
+// As in fa_bwd.hip the two halves run as separate kernels (no location is
+// written by two workgroups; deterministic).
+//
+// All products use v_mfma_f32_16x16x32_{bf16,f16}; P and dS are rounded to
+// the input type before the products that take them.  Lane layouts (lane l,
+// g = l / 16, i = l % 16): A operand A[i][8g + j], B operand B[8g + j][i],
+// result D[4g + r][i] in register r.
+//
+// dK/dV kernel: a workgroup of 8 waves owns 128 keys of one head, 16 per
+// wave as the MFMA columns; it walks the head's query rows in steps of 32.
+//  * S = Q K^T and dP = dO V^T per 16-row block: Q and dO are A operands
+//    read row-major from LDS; K^T and V^T are B operands held in registers
+//    for the whole walk (a lane's 16 bytes are one row of K or V).
+//  * The two 16-row result blocks of S (rows 4g + r and 16 + 4g + r of the
+//    lane's key) are a B operand over the row order {4g..4g+3,
+//    16+4g..16+4g+3}; so dV^T += dO^T P and dK^T += Q^T dS take P and dS
+//    straight from registers, and dO^T, Q^T are read in that order with
+//    ds_read_b64_tr_b16.
+//  * Q and dO of a step are stored twice in LDS, once swizzled for the
+//    row-major reads and once for the transposing reads (each swizzle
+//    conflict-free for its pattern, as in the forward kernels); LDS holds
+//    two steps and each step's loads are issued two steps ahead.
+// dQ kernel: a workgroup of 8 waves owns 128 query rows, 16 per wave as the
+// MFMA columns, and walks the keys in tiles of 64 (computed transposed):
+//  * S^T = K Q^T and dP^T = V dO^T with K and V row-major from LDS and Q^T,
+//    dO^T in registers; each lane holds one query row, so LSE and D are
+//    one register each;
+//  * dQ^T += K^T dS^T with dS^T from registers (the same key-order trick)
+//    and K^T read with ds_read_b64_tr_b16 from a second copy of the K tile.
+// Workgroups of one head are placed on one XCD (see work_item) so that they
+// share the head's tensors through its L2.
+// Under the causal mask (query i at position Nk - N + i) each kernel walks
+// only the blocks some of its rows or keys can see, and a wave skips the
+// steps in which none of its own rows or keys is visible.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
+namespace {
 
-bool bwd_mfma_supported(int, int64_t, int64_t) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-hipError_t launch_bwd_mfma(const BwdArgs &) { return hipErrorInvalidValue; }
+template <typename T> struct Mma;
+template <> struct Mma<bf16_t> {
+    typedef bf16x8 vec;
+    static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma<f16_t> {
+    typedef f16x8 vec;
+    static __device__ __forceinline__ f32x4 run(vec a, vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+
+// LDS swizzles (the forward kernels' conflict-free ones; both have period 16
+// in the row, so a 32- or 64-row tile repeats them).  Row-major copy: 16-byte
+// chunk c of row r at chunk c ^ kswz(r), for reads of rows i, chunks 4 ks +
+// g.  Transposing copy: 8-byte quad u of row r at quad u ^ vswz(r), for
+// ds_read_b64_tr_b16 of rows 4g + i/4, quads 4 db + i%4.
+template <int D> __device__ __forceinline__ int kswz(int r) {
+    if constexpr (D == 64)
+        return ((r >> 2) & 1) | ((__builtin_popcount(r & 15) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+    else return r & 15;
+}
+template <int D> __device__ __forceinline__ int vswz(int r) {
+    if constexpr (D == 64) return 4 * ((r & 3) ^ ((r >> 2) & 1));
+    else return 4 * (r & 7);
+}
+
+// This workgroup's (head, block) in a 1-D grid of nblk * heads workgroups.
+// Workgroup ids are dealt to the 8 XCDs round-robin; when heads is a
+// multiple of 8 the blocks of one head get ids congruent mod 8, so they run
+// on one XCD and share the head's Q, dO (or K, V) through its L2.
+__device__ __forceinline__ void work_item(int nblk, int heads, int &head, int &blk) {
+    const int L = blockIdx.x;
+    if (heads % 8 == 0) {
+        const int local = L / 8;
+        head = (local / nblk) * 8 + L % 8;
+        blk = local % nblk;
+    } else {
+        head = L / nblk;
+        blk = L % nblk;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::vec as_vec(u32x4 x) {
+    return __builtin_bit_cast(typename Mma<T>::vec, x);
+}
+
+// A operand of 16 rows x 32 columns from a row-major (kswz) LDS copy.
+__device__ __forceinline__ u32x4 lds_row16(const unsigned char *base) {
+    return *reinterpret_cast<const u32x4 *>(base);
+}
+
+// A operand of 16 columns x 32 rows (rows in the order {4g..4g+3,
+// 16+4g..16+4g+3}) from a transposing (vswz) LDS copy; `p` is the lane's
+// address in rows 0..15 of the 32-row block.
+template <typename T, int ROWB>
+__device__ __forceinline__ typename Mma<T>::vec lds_tr32(const unsigned char *p) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWB));
+    return __builtin_bit_cast(typename Mma<T>::vec,
+                              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Two 16x16 result blocks (f32) -> one B operand in the input type.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::vec pack_b(f32x4 a, f32x4 b) {
+    typename Mma<T>::vec r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        r[j] = static_cast<T>(a[j]);
+        r[4 + j] = static_cast<T>(b[j]);
+    }
+    return r;
+}
+
+// =============================================================================
+// dK, dV
+// =============================================================================
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_mfma_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
+    T *__restrict__ dk, T *__restrict__ dvo, int N, int Nk, float c, float scale, int heads) {
+    typedef typename Mma<T>::vec vec8;
+    constexpr int KS = D / 32;              // contraction steps over d
+    constexpr int DB = D / 16;              // 16-column blocks of dK^T / dV^T
+    constexpr int ROWB = 2 * D;             // bytes per row
+    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    constexpr int QS = 32;                  // query rows per step
+    constexpr int TILE = QS * ROWB;         // bytes of one 32-row copy
+    constexpr int CH = QS * CPR;            // chunks of one tensor per step
+    constexpr int NL = 2 * CH / kThreads;   // chunks per thread per step (Q and dO)
+    static_assert(NL >= 1 && NL * kThreads == 2 * CH, "load split");
+
+    // Per stage: Q row-major, Q transposing, dO row-major, dO transposing.
+    __shared__ __attribute__((aligned(16))) unsigned char buf[2][4][TILE];
+    __shared__ float s_lse[2][QS];
+    __shared__ float s_D[2][QS];
+
+    int head, kblk;
+    work_item((Nk + kWaves * 16 - 1) / (kWaves * 16), heads, head, kblk);
+    const int j0 = kblk * (kWaves * 16);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64;
+    const int g = lane / 16;
+    const int li = lane % 16;
+    const int kw0 = j0 + wave * 16;
+    const int key = kw0 + li;               // this lane's key (MFMA column)
+
+    const T *qh = q + (int64_t)head * N * D;
+    const T *dh = dout + (int64_t)head * N * D;
+    const float *Lh = lse + (int64_t)head * N;
+    const float *Dh = Dsum + (int64_t)head * N;
+    const auto qrs = make_rsrc(qh, (uint32_t)N * D * 2u);
+    const auto drs = make_rsrc(dh, (uint32_t)N * D * 2u);
+    const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const auto vrs = make_rsrc(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+
+    // K^T and V^T B operands: lane holds row `key`, columns 32 ks + 8g .. +7.
+    vec8 kop[KS], vop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = ((uint32_t)key * D + ks * 32 + 8 * g) * 2u;
+        kop[ks] = as_vec<T>(buffer_load16(krs, off));
+        vop[ks] = as_vec<T>(buffer_load16(vrs, off));
+    }
+
+    // Steps over query rows: all rows, or (causal) from the first row that
+    // sees key j0.
+    const int off_c = Nk - N;
+    const int first = CAUSAL ? max(0, j0 - off_c) : 0;
+    const int s0 = first / QS;
+    const int nsteps = (N + QS - 1) / QS - s0;
+
+    // Per-thread load slots: chunk t * kThreads + tid of [Q chunks | dO chunks].
+    uint32_t gofs[NL], wA[NL], wT[NL];
+    bool isdo[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+        const int cidx = t * kThreads + tid;
+        isdo[t] = cidx >= CH;
+        const int ch = cidx % CH;
+        const int row = ch / CPR, cc = ch % CPR;
+        gofs[t] = ((uint32_t)row * D + cc * 8) * 2u;
+        wA[t] = row * ROWB + ((cc ^ kswz<D>(row)) * 16);
+        wT[t] = row * ROWB + (((2 * cc) ^ vswz<D>(row)) * 8);
+    }
+    // Per-lane read offsets.
+    uint32_t rA[KS], rT[DB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rA[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int r0 = 4 * g + li / 4;
+        rT[db] = r0 * ROWB + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+    }
+
+    // Steps are fetched two ahead: step x's data waits in register set x % 2
+    // until it is stored to LDS stage x % 2 at the end of step x - 1.
+    u32x4 regs0[NL], regs1[NL];
+    float val0 = 0.f, val1 = 0.f;
+    auto load_step = [&](u32x4 (&rg)[NL], float &val, int s) {   // global -> registers
+        const uint32_t base = (uint32_t)((s0 + s) * QS) * D * 2u;
+#pragma unroll
+        for (int t = 0; t < NL; ++t)
+            rg[t] = isdo[t] ? buffer_load16(drs, base + gofs[t]) : buffer_load16(qrs, base + gofs[t]);
+        if (tid < 2 * QS) {
+            const int row = (s0 + s) * QS + (tid % QS);
+            if (tid < QS) {
+                const float L = row < N ? Lh[row] : -INFINITY;
+                val = L == -INFINITY ? INFINITY : L * kLog2e;   // +inf: no weight
+            } else {
+                val = row < N ? Dh[row] : 0.f;
+            }
+        }
+    };
+    auto store_step = [&](const u32x4 (&rg)[NL], float val, int st) {   // registers -> LDS
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            unsigned char *a = buf[st][isdo[t] ? 2 : 0];
+            unsigned char *b = buf[st][isdo[t] ? 3 : 1];
+            *reinterpret_cast<u32x4 *>(a + wA[t]) = rg[t];
+            *reinterpret_cast<u32x4 *>(b + wT[t]) = rg[t];
+        }
+        if (tid < QS) s_lse[st][tid] = val;
+        else if (tid < 2 * QS) s_D[st][tid - QS] = val;
+    };
+
+    f32x4 dka[DB], dva[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dka[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dva[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto compute = [&](int s, int st) {
+        const int i0 = (s0 + s) * QS;
+        // Skip when no row of this step sees any of the wave's keys.
+        const bool active = !CAUSAL || kw0 <= off_c + i0 + QS - 1;
+        if (active) {
+            const unsigned char *qa = buf[st][0], *qt = buf[st][1];
+            const unsigned char *da = buf[st][2], *dt = buf[st][3];
+            f32x4 S[2], dP[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dP[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWB + rA[ks])), kop[ks], S[rb]);
+                    dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWB + rA[ks])), vop[ks], dP[rb]);
+                }
+            }
+            // P and dS of rows rb*16 + 4g + r, key `key`.
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rl = rb * 16 + 4 * g + r;
+                    const int row = i0 + rl;
+                    const bool vis = key < Nk && (!CAUSAL || key <= off_c + row);
+                    const float p = vis ? fast_exp2(fmaf(S[rb][r], c, -s_lse[st][rl])) : 0.f;
+                    S[rb][r] = p;
+                    dP[rb][r] = p * (dP[rb][r] - s_D[st][rl]);
+                }
+            const vec8 pb = pack_b<T>(S[0], S[1]);
+            const vec8 sb = pack_b<T>(dP[0], dP[1]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dva[db] = Mma<T>::run(lds_tr32<T, ROWB>(dt + rT[db]), pb, dva[db]);
+                dka[db] = Mma<T>::run(lds_tr32<T, ROWB>(qt + rT[db]), sb, dka[db]);
+            }
+        }
+    };
+
+    if (nsteps > 0) {
+        load_step(regs0, val0, 0);
+        store_step(regs0, val0, 0);
+    }
+    if (nsteps > 1) load_step(regs1, val1, 1);
+    __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {
+        if (s + 2 < nsteps) load_step(regs0, val0, s + 2);
+        compute(s, 0);
+        if (s + 1 < nsteps) store_step(regs1, val1, 1);
+        __syncthreads();
+        if (s + 1 >= nsteps) break;
+        if (s + 3 < nsteps) load_step(regs1, val1, s + 3);
+        compute(s + 1, 1);
+        if (s + 2 < nsteps) store_step(regs0, val0, 0);
+        __syncthreads();
+    }
+
+    // dK^T, dV^T result blocks: lane holds columns 16 db + 4g + r of `key`.
+    if (key < Nk) {
+        T *dkr = dk + ((int64_t)head * Nk + key) * D;
+        T *dvr = dvo + ((int64_t)head * Nk + key) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            t4 a, b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                a[r] = static_cast<T>(dka[db][r] * scale);
+                b[r] = static_cast<T>(dva[db][r]);
+            }
+            *reinterpret_cast<t4 *>(dkr + 16 * db + 4 * g) = a;
+            *reinterpret_cast<t4 *>(dvr + 16 * db + 4 * g) = b;
+        }
+    }
+}
+
+// =============================================================================
+// dQ
+// =============================================================================
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_mfma_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
+    T *__restrict__ dq, int N, int Nk, float c, float scale, int heads) {
+    typedef typename Mma<T>::vec vec8;
+    constexpr int KS = D / 32;
+    constexpr int DB = D / 16;
+    constexpr int ROWB = 2 * D;
+    constexpr int CPR = ROWB / 16;
+    constexpr int BC = 64;                  // keys per step
+    constexpr int TILE = BC * ROWB;
+    constexpr int CH = BC * CPR;            // chunks of one tensor per step
+    constexpr int NL = 2 * CH / kThreads;   // chunks per thread per step (K and V)
+    static_assert(NL >= 1 && NL * kThreads == 2 * CH, "load split");
+
+    // Per stage: K row-major, K transposing, V row-major.
+    __shared__ __attribute__((aligned(16))) unsigned char buf[2][3][TILE];
+
+    int head, qblk;
+    work_item((N + kWaves * 16 - 1) / (kWaves * 16), heads, head, qblk);
+    const int i0 = qblk * (kWaves * 16);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64;
+    const int g = lane / 16;
+    const int li = lane % 16;
+    const int qw0 = i0 + wave * 16;
+    const int row = qw0 + li;               // this lane's query row (MFMA column)
+
+    const auto qrs = make_rsrc(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
+    const auto drs = make_rsrc(dout + (int64_t)head * N * D, (uint32_t)N * D * 2u);
+    const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const auto vrs = make_rsrc(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+
+    vec8 qop[KS], dop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t off = ((uint32_t)row * D + ks * 32 + 8 * g) * 2u;
+        qop[ks] = as_vec<T>(buffer_load16(qrs, off));
+        dop[ks] = as_vec<T>(buffer_load16(drs, off));
+    }
+    float lse2 = INFINITY, Drow = 0.f;
+    if (row < N) {
+        const float L = lse[(int64_t)head * N + row];
+        lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
+        Drow = Dsum[(int64_t)head * N + row];
+    }
+
+    const int off_c = Nk - N;
+    const int key_end = CAUSAL ? min(Nk, off_c + min(i0 + kWaves * 16, N)) : Nk;
+    const int nsteps = key_end > 0 ? (key_end + BC - 1) / BC : 0;
+
+    uint32_t gofs[NL], wA[NL], wT[NL];
+    bool isv[NL];
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+        const int cidx = t * kThreads + tid;
+        isv[t] = cidx >= CH;
+        const int ch = cidx % CH;
+        const int r = ch / CPR, cc = ch % CPR;
+        gofs[t] = ((uint32_t)r * D + cc * 8) * 2u;
+        wA[t] = r * ROWB + ((cc ^ kswz<D>(r)) * 16);
+        wT[t] = r * ROWB + (((2 * cc) ^ vswz<D>(r)) * 8);
+    }
+    uint32_t rA[KS], rT[DB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rA[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int r0 = 4 * g + li / 4;
+        rT[db] = r0 * ROWB + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+    }
+
+    u32x4 regs0[NL], regs1[NL];
+    auto load_step = [&](u32x4 (&rg)[NL], int s) {
+        const uint32_t base = (uint32_t)(s * BC) * D * 2u;
+#pragma unroll
+        for (int t = 0; t < NL; ++t)
+            rg[t] = isv[t] ? buffer_load16(vrs, base + gofs[t]) : buffer_load16(krs, base + gofs[t]);
+    };
+    auto store_step = [&](const u32x4 (&rg)[NL], int st) {
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            if (isv[t]) {
+                *reinterpret_cast<u32x4 *>(buf[st][2] + wA[t]) = rg[t];
+            } else {
+                *reinterpret_cast<u32x4 *>(buf[st][0] + wA[t]) = rg[t];
+                *reinterpret_cast<u32x4 *>(buf[st][1] + wT[t]) = rg[t];
+            }
+        }
+    };
+
+    f32x4 dqa[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int s, int st) {
+        const int j0 = s * BC;
+        const bool active = qw0 < N && (!CAUSAL || j0 <= off_c + qw0 + 15);
+        if (active) {
+            const unsigned char *ka = buf[st][0], *kt = buf[st][1], *va = buf[st][2];
+            f32x4 S[4], dP[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dP[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    S[kb] = Mma<T>::run(as_vec<T>(lds_row16(ka + kb * 16 * ROWB + rA[ks])), qop[ks], S[kb]);
+                    dP[kb] = Mma<T>::run(as_vec<T>(lds_row16(va + kb * 16 * ROWB + rA[ks])), dop[ks], dP[kb]);
+                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = j0 + kb * 16 + 4 * g + r;
+                    const bool vis = key < Nk && (!CAUSAL || key <= off_c + row);
+                    const float p = vis ? fast_exp2(fmaf(S[kb][r], c, -lse2)) : 0.f;
+                    dP[kb][r] = p * (dP[kb][r] - Drow);
+                }
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
+                const vec8 sb = pack_b<T>(dP[2 * pc], dP[2 * pc + 1]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    dqa[db] = Mma<T>::run(lds_tr32<T, ROWB>(kt + pc * 32 * ROWB + rT[db]), sb, dqa[db]);
+            }
+        }
+    };
+
+    // Steps fetched two ahead, as in the dK/dV kernel.
+    if (nsteps > 0) {
+        load_step(regs0, 0);
+        store_step(regs0, 0);
+    }
+    if (nsteps > 1) load_step(regs1, 1);
+    __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {
+        if (s + 2 < nsteps) load_step(regs0, s + 2);
+        compute(s, 0);
+        if (s + 1 < nsteps) store_step(regs1, 1);
+        __syncthreads();
+        if (s + 1 >= nsteps) break;
+        if (s + 3 < nsteps) load_step(regs1, s + 3);
+        compute(s + 1, 1);
+        if (s + 2 < nsteps) store_step(regs0, 0);
+        __syncthreads();
+    }
+
+    if (row < N) {
+        T *dqr = dq + ((int64_t)head * N + row) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            t4 a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = static_cast<T>(dqa[db][r] * scale);
+            *reinterpret_cast<t4 *>(dqr + 16 * db + 4 * g) = a;
+        }
+    }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch3(const BwdArgs &b) {
+    const FwdArgs &a = b.a;
+    const unsigned heads = (unsigned)(a.B * a.H);
+    const float c = a.scale * kLog2e;
+    const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAUSAL>), gk, dim3(kThreads), 0, a.stream,
+                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                       static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
+                       b.Dsum, static_cast<T *>(b.dk), static_cast<T *>(b.dv), (int)a.N,
+                       (int)a.Nk, c, a.scale, (int)heads);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAUSAL>), gq, dim3(kThreads), 0, a.stream,
+                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                       static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
+                       b.Dsum, static_cast<T *>(b.dq), (int)a.N, (int)a.Nk, c, a.scale,
+                       (int)heads);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch2(const BwdArgs &b) {
+    return b.a.causal ? launch3<T, D, true>(b) : launch3<T, D, false>(b);
+}
+
+template <typename T>
+hipError_t launch1(const BwdArgs &b) {
+    return b.a.d == 64 ? launch2<T, 64>(b) : launch2<T, 128>(b);
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(int dtype, int64_t d, int64_t dv) {
+    return (dtype == kBF16 || dtype == kF16) && d == dv && (d == 64 || d == 128);
+}
+
+hipError_t launch_bwd_mfma(const BwdArgs &b) {
+    if (!bwd_mfma_supported(b.a.dtype, b.a.d, b.a.dv)) return hipErrorInvalidValue;
+    return b.a.dtype == kBF16 ? launch1<bf16_t>(b) : launch1<f16_t>(b);
+}
 
 }  // namespace fa
