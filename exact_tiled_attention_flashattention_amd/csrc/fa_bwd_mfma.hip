@@ -69,6 +69,8 @@ template <> struct Mma<f16_t> {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+// __launch_bounds__' second argument is the minimum waves per SIMD: 4 (two
+// resident workgroups per CU, at most 128 registers) for d = 64, 2 for d = 128.
 
 // LDS swizzles (the forward kernels' conflict-free ones; both have period 16
 // in the row, so a 32- or 64-row tile repeats them).  Row-major copy: 16-byte
@@ -138,7 +140,7 @@ __device__ __forceinline__ typename Mma<T>::vec pack_b(f32x4 a, f32x4 b) {
 // dK, dV
 // =============================================================================
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
     T *__restrict__ dk, T *__restrict__ dvo, int N, int Nk, float c, float scale, int heads) {
@@ -273,18 +275,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_mfma_kernel(
                     dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWB + rA[ks])), vop[ks], dP[rb]);
                 }
             }
-            // P and dS of rows rb*16 + 4g + r, key `key`.
+            // P and dS of rows rb*16 + 4g + r, key `key`.  Only steps where
+            // some of the wave's keys are hidden from some row (the diagonal,
+            // or keys past Nk) pay for the mask.
+            const bool masked = kw0 + 15 >= Nk || (CAUSAL && kw0 + 15 > off_c + i0);
+            if (masked) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rl = rb * 16 + 4 * g + r;
-                    const int row = i0 + rl;
-                    const bool vis = key < Nk && (!CAUSAL || key <= off_c + row);
-                    const float p = vis ? fast_exp2(fmaf(S[rb][r], c, -s_lse[st][rl])) : 0.f;
-                    S[rb][r] = p;
-                    dP[rb][r] = p * (dP[rb][r] - s_D[st][rl]);
-                }
+                    for (int r = 0; r < 4; ++r) {
+                        const int rl = rb * 16 + 4 * g + r;
+                        const bool vis = key < Nk && (!CAUSAL || key <= off_c + i0 + rl);
+                        const float p = vis ? fast_exp2(fmaf(S[rb][r], c, -s_lse[st][rl])) : 0.f;
+                        S[rb][r] = p;
+                        dP[rb][r] = p * (dP[rb][r] - s_D[st][rl]);
+                    }
+            } else {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int rl = rb * 16 + 4 * g + r;
+                        const float p = fast_exp2(fmaf(S[rb][r], c, -s_lse[st][rl]));
+                        S[rb][r] = p;
+                        dP[rb][r] = p * (dP[rb][r] - s_D[st][rl]);
+                    }
+            }
             const vec8 pb = pack_b<T>(S[0], S[1]);
             const vec8 sb = pack_b<T>(dP[0], dP[1]);
 #pragma unroll
@@ -336,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_mfma_kernel(
 // dQ
 // =============================================================================
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
     T *__restrict__ dq, int N, int Nk, float c, float scale, int heads) {
@@ -448,15 +464,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_mfma_kernel(
                     dP[kb] = Mma<T>::run(as_vec<T>(lds_row16(va + kb * 16 * ROWB + rA[ks])), dop[ks], dP[kb]);
                 }
             }
+            // As in the dK/dV kernel, only steps that reach past some row's
+            // last visible key (or past Nk) apply the mask.
+            const bool masked = j0 + BC > Nk || (CAUSAL && j0 + BC - 1 > off_c + qw0);
+            if (masked) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = j0 + kb * 16 + 4 * g + r;
-                    const bool vis = key < Nk && (!CAUSAL || key <= off_c + row);
-                    const float p = vis ? fast_exp2(fmaf(S[kb][r], c, -lse2)) : 0.f;
-                    dP[kb][r] = p * (dP[kb][r] - Drow);
-                }
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = j0 + kb * 16 + 4 * g + r;
+                        const bool vis = key < Nk && (!CAUSAL || key <= off_c + row);
+                        const float p = vis ? fast_exp2(fmaf(S[kb][r], c, -lse2)) : 0.f;
+                        dP[kb][r] = p * (dP[kb][r] - Drow);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float p = fast_exp2(fmaf(S[kb][r], c, -lse2));
+                        dP[kb][r] = p * (dP[kb][r] - Drow);
+                    }
+            }
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc) {
                 const vec8 sb = pack_b<T>(dP[2 * pc], dP[2 * pc + 1]);
