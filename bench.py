@@ -201,6 +201,9 @@ def summarize_trace(directory: str) -> None:
     gqa_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_gqa -o run -- "
                "python $R/bench.py --only gqa   (run from /tmp, repo at $R; 50 timed + 10 warm-up "
                "fa_decode_splitkv_gqa calls)")
+    bwd_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_bwd -o run -- "
+               "python $R/bench.py --only bwd   (run from /tmp, repo at $R; 50 timed + 10 warm-up "
+               "fa_bwd calls)")
     # file -> (kernel that must be in the trace, kernels listed, command)
     groups = {
         f"fwd_mfma_kernel_{PREFILL}.txt": ("fwd_mfma_kernel", ("fwd_mfma_kernel",), default_cmd),
@@ -210,10 +213,14 @@ def summarize_trace(directory: str) -> None:
         f"decode_splitkv_gqa_{GQA_WORKLOAD}.txt": ("decode_segment_mfma_kernel",
                                                    ("decode_segment_mfma_kernel",
                                                     "decode_merge_kernel"), gqa_cmd),
+        f"bwd_mfma_{PREFILL}.txt": ("bwd_dkdv_mfma_kernel",
+                                    ("bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel",
+                                     "bwd_dot_kernel"), bwd_cmd),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for fname, (primary, keys, cmd) in groups.items():
-        if not any(primary in r["Name"] for r in rows):
+        # Only the run that times this entry point (a run may launch others once).
+        if not any(primary in r["Name"] and int(r["Calls"]) >= 10 for r in rows):
             continue
         lines = [f"# rocprofv3 kernel-trace statistics, {fname[:-4]}",
                  f"# command: {cmd}",
