@@ -355,7 +355,7 @@ def split_sweep(args, torch, fa) -> int:
             ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
             times[S] = ms[len(ms) // 2] * 1e3
         best = min(times, key=times.get)
-        auto = fa.decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, q.dtype)
+        auto = fa.decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, d, q.dtype)
         cells = " ".join(f"{times[c]:.1f}" if c in times else "-" for c in SPLIT_CANDIDATES)
         rel = times[auto] / times[best] if auto in times else float("nan")
         line = f"{B} {Hq} {Hkv} {N} {Nk} | {cells} | {best} | {auto} ({rel:.3f})"
@@ -418,6 +418,59 @@ def bench_bwd(args, torch, fa, si, dev) -> int:
     return 0
 
 
+def _time_call(torch, call, steps, warmup, stream):
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        ev[i].record(stream)
+        call()
+    ev[steps].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ms[len(ms) // 2] * 1e-3   # median seconds
+
+
+def bench_dims(args, torch, fa, si, dev) -> int:
+    """Head dimensions outside d = dv in {64, 128}: causal bf16 prefill
+    (B16 x H16 x 2048) and decode (B8 x H32 x 32768, 64 splits) for several
+    (d, dv), next to d = dv = 128 on the matrix cores.  One JSON line with a
+    case list; TFLOP/s credited as 2 N Nk (d + dv) per head, halved for
+    causal; decode GB/s over K, V once plus q, o, lse."""
+    stream = torch.cuda.current_stream(dev)
+    cases = []
+    for d, dv in [(128, 128), (64, 128), (128, 64), (256, 256)]:
+        B, H, N = 16, 16, 2048
+        q, k, v = si.device_qkv(si.Shape(B, H, N, N, d, dv), 11, "bf16", dev, 1.0)
+        sc = 1.0 / math.sqrt(d)
+        t = _time_call(torch, lambda: fa.fwd(q, k, v, causal=True, scale=sc), args.steps,
+                       args.warmup, stream)
+        flop = 2.0 * N * N * (d + dv) * B * H / 2
+        cases.append({"entry": "fa_fwd", "B": B, "H": H, "N": N, "d": d, "dv": dv,
+                      "causal": True, "us": round(t * 1e6, 1),
+                      "tflops": round(flop / t / 1e12, 1),
+                      "frac_bf16_peak": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        del q, k, v
+    for d, dv in [(128, 128), (64, 128), (256, 256)]:
+        B, H, Nk, S = 8, 32, 32768, 64
+        q, k, v = si.device_qkv(si.Shape(B, H, 1, Nk, d, dv), 12, "bf16", dev, 1.0)
+        ws = torch.empty(fa.decode_splitkv_workspace_size(B, H, 1, dv, S), dtype=torch.uint8,
+                         device=dev)
+        t = _time_call(torch, lambda: fa.decode_splitkv(q, k, v, num_splits=S, workspace=ws),
+                       args.steps, args.warmup, stream)
+        nbytes = B * H * (Nk * (d + dv) * 2 + d * 2 + dv * 2 + 4)
+        cases.append({"entry": "fa_decode_splitkv", "B": B, "H": H, "Nk": Nk, "d": d, "dv": dv,
+                      "splits": S, "us": round(t * 1e6, 1), "gbs": round(nbytes / t / 1e9, 1),
+                      "frac_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)})
+        del q, k, v
+    print(json.dumps({"metric": "head-dimension coverage (median of HIP-event timings)",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+                      "data": "synthetic (seeded torch Philox draws on the GPU)",
+                      "cases": cases}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -428,10 +481,10 @@ def main() -> int:
                     help="prefill heads the CPU oracle is timed on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="add one plain 1 GiB device copy per step (for counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "gqa", "bwd"],
+    ap.add_argument("--only", choices=["prefill", "decode", "gqa", "bwd", "dims"],
                     help="profile one entry point alone (the JSON line then omits the other); "
-                         "'gqa' times the grouped-query decode, 'bwd' the backward (neither is "
-                         "part of the default line)")
+                         "'gqa' times the grouped-query decode, 'bwd' the backward, 'dims' "
+                         "other head dimensions (none of these is part of the default line)")
     ap.add_argument("--split-sweep", action="store_true",
                     help="time decode at every candidate split count over a set of shapes "
                          "and write the table under profiles/")
@@ -465,6 +518,8 @@ def main() -> int:
         return bench_gqa(args, torch, fa, si, dev)
     if args.only == "bwd":
         return bench_bwd(args, torch, fa, si, dev)
+    if args.only == "dims":
+        return bench_dims(args, torch, fa, si, dev)
     if args.split_sweep:
         return split_sweep(args, torch, fa)
     wp = si.WORKLOADS[PREFILL]

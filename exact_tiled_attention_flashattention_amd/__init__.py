@@ -62,7 +62,7 @@ def library() -> ctypes.CDLL:
                                           c_int, ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t,
                                           vp]
     lib.fa_decode_splitkv_gqa.restype = c_int
-    lib.fa_decode_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, i64, i64, c_int]
+    lib.fa_decode_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, i64, i64, i64, c_int]
     lib.fa_decode_splitkv_auto_splits.restype = c_int
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
@@ -182,12 +182,12 @@ def decode_splitkv_workspace_size(B: int, H: int, N: int, dv: int, num_splits: i
     return int(library().fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits))
 
 
-def decode_splitkv_auto_splits(B: int, Hq: int, Hkv: int, N: int, Nk: int, d: int,
+def decode_splitkv_auto_splits(B: int, Hq: int, Hkv: int, N: int, Nk: int, d: int, dv: int,
                                dtype: torch.dtype) -> int:
     """The split count ``num_splits=0`` selects (``fa_decode_splitkv_auto_splits``)."""
-    n = int(library().fa_decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, _DTYPE_CODE[dtype]))
+    n = int(library().fa_decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dv, _DTYPE_CODE[dtype]))
     if n < 1:
-        raise ValueError(f"no split count for B={B} Hq={Hq} Hkv={Hkv} N={N} Nk={Nk} d={d}")
+        raise ValueError(f"no split count for B={B} Hq={Hq} Hkv={Hkv} N={N} Nk={Nk} d={d} dv={dv}")
     return n
 
 
@@ -211,7 +211,7 @@ def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if workspace is None:
-        splits = num_splits or decode_splitkv_auto_splits(B, H, H, N, Nk, d, q.dtype)
+        splits = num_splits or decode_splitkv_auto_splits(B, H, H, N, Nk, d, dv, q.dtype)
         nbytes = decode_splitkv_workspace_size(B, H, N, dv, splits)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = library().fa_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -242,7 +242,7 @@ def decode_splitkv_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     if workspace is None:
-        splits = num_splits or decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, q.dtype)
+        splits = num_splits or decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dv, q.dtype)
         nbytes = decode_splitkv_workspace_size(B, Hq, N, dv, splits)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     st = library().fa_decode_splitkv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

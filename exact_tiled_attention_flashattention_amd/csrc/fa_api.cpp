@@ -27,9 +27,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t *out) {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-bool supported_dims(int64_t d, int64_t dv) {
-    return d == dv && (d == 32 || d == 64 || d == 128);
-}
+bool supported_dim(int64_t x) { return x == 32 || x == 64 || x == 128 || x == 256; }
+bool supported_dims(int64_t d, int64_t dv) { return supported_dim(d) && supported_dim(dv); }
 
 // Checks shared by both entry points.  Order: invalid arguments first, then
 // the support matrix.
@@ -100,9 +99,10 @@ constexpr int64_t kAutoWorkgroups = 512;
 constexpr int64_t kAutoMinKeys = 256;
 constexpr int kAutoMaxSplits = 256;
 
-int auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk, int dtype) {
+int auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk, int64_t d, int64_t dv,
+                int dtype) {
     const int64_t rows = (Hq / Hkv) * N;
-    const int64_t units = fa::decode_workgroups_per_split(dtype, B, Hkv, rows);
+    const int64_t units = fa::decode_workgroups_per_split(dtype, d, dv, B, Hkv, rows);
     int S = 1;
     while (S < kAutoMaxSplits && units * S < kAutoWorkgroups && Nk >= 2 * S * kAutoMinKeys) S *= 2;
     return S;
@@ -130,8 +130,8 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, void *o, float *
     fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, stream);
     (void)hipGetLastError();   // clear any stale error so it is not reported as ours
     hipError_t e = !fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_rowwise(a)
-                   : d == 64                                    ? fa::launch_fwd_mfma_d64(a)
-                                                                : fa::launch_fwd_mfma_d128(a);
+                   : (d == 128 && dv == 128)                    ? fa::launch_fwd_mfma_d128(a)
+                                                                : fa::launch_fwd_mfma16(a);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -158,7 +158,7 @@ fa_status_t decode_impl(const void *q, const void *k, const void *v, void *o, fl
     if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
     fa_status_t st = check_common(q, k, v, o, lse, B, Hq, N, Nk, d, dv, scale, dtype);
     if (st != FA_OK) return st;
-    if (num_splits == 0) num_splits = auto_splits(B, Hq, Hkv, N, Nk, dtype);
+    if (num_splits == 0) num_splits = auto_splits(B, Hq, Hkv, N, Nk, d, dv, dtype);
     // Launch-shape limits of the segment kernel: (segment, key/value head,
     // row group of up to 8 of the (Hq / Hkv) x N rows).
     const int64_t rows = (Hq / Hkv) * N;
@@ -237,13 +237,13 @@ fa_status_t fa_bwd(const void *q, const void *k, const void *v, const void *o, c
 }
 
 int fa_decode_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk,
-                                  int64_t d, fa_dtype_t dtype) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || Nk < 1 || d < 1 ||
+                                  int64_t d, int64_t dv, fa_dtype_t dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N < 1 || Nk < 1 || d < 1 || dv < 1 ||
         !valid_dtype(dtype))
         return 0;
     int64_t t;
     if (!mul_ok(B, Hq, &t) || t > kMaxI32 || !mul_ok(Hq / Hkv, N, &t) || t > kMaxI32) return 0;
-    return auto_splits(B, Hq, Hkv, N, Nk, dtype);
+    return auto_splits(B, Hq, Hkv, N, Nk, d, dv, dtype);
 }
 
 const char *fa_status_string(fa_status_t status) {

@@ -16,7 +16,8 @@
 // deterministic.  The price is that S, P and dP are recomputed in both.
 //
 // The VALU kernels here serve fp32 (whose 2e-5 bar needs fp32 operands) and
-// every shape the matrix-core kernels do not take: one wave per query row
+// every (d, dv) the matrix-core kernels do not take (d, dv in {32, 64, 128,
+// 256}, dv may differ from d): one wave per query row
 // (dQ) or per key (dK, dV), the head dimension spread over the lanes, dot
 // products summed over the wave.
 #include "fa_device.h"
@@ -184,12 +185,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_rowwise_kernel(
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 hipError_t launch_rowwise(const BwdArgs &b) {
     const FwdArgs &a = b.a;
     const int64_t heads = a.B * a.H;
     const unsigned gq = (unsigned)((heads * a.N + 3) / 4);
-    hipLaunchKernelGGL((bwd_dq_rowwise_kernel<T, D, D>), dim3(gq), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dq_rowwise_kernel<T, D, DV>), dim3(gq), dim3(256), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        b.Dsum, static_cast<T *>(b.dq), heads, (int)a.N, (int)a.Nk, a.causal,
@@ -197,12 +198,23 @@ hipError_t launch_rowwise(const BwdArgs &b) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gk = (unsigned)((heads * a.Nk + 3) / 4);
-    hipLaunchKernelGGL((bwd_dkdv_rowwise_kernel<T, D, D>), dim3(gk), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_rowwise_kernel<T, D, DV>), dim3(gk), dim3(256), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        b.Dsum, static_cast<T *>(b.dk), static_cast<T *>(b.dv), heads,
                        (int)a.N, (int)a.Nk, a.causal, a.scale);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_rowwise_dv(const BwdArgs &b) {
+    switch (b.a.dv) {
+        case 32: return launch_rowwise<T, D, 32>(b);
+        case 64: return launch_rowwise<T, D, 64>(b);
+        case 128: return launch_rowwise<T, D, 128>(b);
+        case 256: return launch_rowwise<T, D, 256>(b);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename T, int DV>
@@ -219,14 +231,17 @@ hipError_t launch_dot(const BwdArgs &b) {
 template <typename T>
 hipError_t launch_typed(const BwdArgs &b) {
     const FwdArgs &a = b.a;
-    hipError_t e = a.dv == 32 ? launch_dot<T, 32>(b) : a.dv == 64 ? launch_dot<T, 64>(b)
-                                                                  : launch_dot<T, 128>(b);
+    hipError_t e = a.dv == 32    ? launch_dot<T, 32>(b)
+                   : a.dv == 64  ? launch_dot<T, 64>(b)
+                   : a.dv == 128 ? launch_dot<T, 128>(b)
+                                 : launch_dot<T, 256>(b);
     if (e != hipSuccess) return e;
     if (bwd_mfma_supported(a.dtype, a.d, a.dv)) return launch_bwd_mfma(b);
     switch (a.d) {
-        case 32: return launch_rowwise<T, 32>(b);
-        case 64: return launch_rowwise<T, 64>(b);
-        case 128: return launch_rowwise<T, 128>(b);
+        case 32: return launch_rowwise_dv<T, 32>(b);
+        case 64: return launch_rowwise_dv<T, 64>(b);
+        case 128: return launch_rowwise_dv<T, 128>(b);
+        case 256: return launch_rowwise_dv<T, 256>(b);
         default: return hipErrorInvalidValue;
     }
 }

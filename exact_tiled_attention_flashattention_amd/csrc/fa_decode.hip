@@ -17,10 +17,13 @@
 // group instead of once per query head.
 //
 // Segment kernel mapping (one workgroup of 4 waves per (segment, key/value
-// head, row group), rows counted over the G query heads x N queries): a key row of D elements is read as 16-byte pieces by LPK
-// consecutive lanes (bf16/fp16 d=128: 16 lanes), so one load instruction of
-// a wave covers KPL = 64/LPK consecutive keys -- a contiguous 1 KiB of K or
-// V.  Each "key slot" (group of LPK lanes) keeps its own online-softmax
+// head, row group), rows counted over the G query heads x N queries): a key
+// is served by LPK consecutive lanes, each holding one 16-byte piece of its
+// K row and one of its V row (bf16/fp16 d = dv = 128: 16 lanes; with
+// d != dv, LPK covers the longer row and the other row uses the first
+// lanes), so one load instruction of a wave covers KPL = 64/LPK
+// consecutive keys -- contiguous K or V rows.  Each "key slot" (group of
+// LPK lanes) keeps its own online-softmax
 // state (m, l, o) for every query row it serves, so the loop needs no
 // cross-slot exchange; the dot product of a key is summed over its LPK
 // lanes with DPP.  At the end the 4 waves x KPL slot states are merged
@@ -39,13 +42,15 @@ constexpr int kUnroll = 8;   // loads of K (and of V) in flight per lane per ste
 // A buffer offset beyond any head's K/V extent (at most 2^31 bytes).
 constexpr uint32_t kOutOfRange = 0xC0000000u;
 
-template <typename T, int D, int R>
+template <typename T, int D, int DV, int R>
 __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int N, int Nk, int causal,
     float scale_log2, int num_splits, int seg_len, int G) {
     constexpr int EPL = 16 / (int)sizeof(T);   // elements per 16-byte piece
-    constexpr int LPK = D / EPL;               // lanes per key row
+    constexpr int KP = D / EPL;                // pieces of a K row
+    constexpr int VP = DV / EPL;               // pieces of a V row
+    constexpr int LPK = KP > VP ? KP : VP;     // lanes per key
     constexpr int KPL = 64 / LPK;              // keys per wave load
     constexpr int KEYS_PER_STEP = KPL * kUnroll;
     static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "bad key-row split");
@@ -57,10 +62,11 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     const int wave = tid / 64;
     const int lane = tid % 64;
     const int slot = lane / LPK;   // which key of a wave load this lane serves
-    const int t = lane % LPK;      // which 16-byte piece of the row
+    const int t = lane % LPK;      // which 16-byte piece of the K and V rows
+    const bool has_k = t < KP, has_v = t < VP;   // (with d != dv some lanes hold one only)
 
     const T *kh = k + (int64_t)kvh * Nk * D;
-    const T *vh = v + (int64_t)kvh * Nk * D;
+    const T *vh = v + (int64_t)kvh * Nk * DV;
 
     // Query pieces of the R rows served by this workgroup.  Row x of the
     // group is query x % N of query head kvh * G + x / N; rows past G * N
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
         const int row = ok ? x % N : 0;
         const int64_t qhead = (int64_t)kvh * G + (ok ? x / N : 0);
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (ok) raw = *reinterpret_cast<const u32x4 *>(q + (qhead * N + row) * D + t * EPL);
+        if (ok && has_k) raw = *reinterpret_cast<const u32x4 *>(q + (qhead * N + row) * D + t * EPL);
         const T *e = reinterpret_cast<const T *>(&raw);
 #pragma unroll
         for (int i = 0; i < EPL; ++i) qr[r][i] = to_f32(e[i]);
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     // Bounds-checked views of this head's K and V: keys past the segment
     // are pointed outside them and read as zeros, so the loads need no branch.
     const auto krs = make_rsrc(kh, (uint32_t)Nk * D * (uint32_t)sizeof(T));
-    const auto vrs = make_rsrc(vh, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+    const auto vrs = make_rsrc(vh, (uint32_t)Nk * DV * (uint32_t)sizeof(T));
 
     // Waves take consecutive steps of KEYS_PER_STEP keys round-robin.
     for (int base = seg_begin + wave * KEYS_PER_STEP; base < seg_end;
@@ -105,11 +111,13 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int key = base + u * KPL + slot;
-            const uint32_t off = key < seg_end
-                                     ? ((uint32_t)key * D + t * EPL) * (uint32_t)sizeof(T)
-                                     : kOutOfRange;
-            kraw[u] = buffer_load16_nt(krs, off);
-            vraw[u] = buffer_load16_nt(vrs, off);
+            const bool in = key < seg_end;
+            const uint32_t koff = in && has_k ? ((uint32_t)key * D + t * EPL) * (uint32_t)sizeof(T)
+                                              : kOutOfRange;
+            const uint32_t voff = in && has_v ? ((uint32_t)key * DV + t * EPL) * (uint32_t)sizeof(T)
+                                              : kOutOfRange;
+            kraw[u] = buffer_load16_nt(krs, koff);
+            vraw[u] = buffer_load16_nt(vrs, voff);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
     constexpr int STATES = kWaves * KPL;
     __shared__ float sm_m[R][STATES];
     __shared__ float sm_l[R][STATES];
-    __shared__ float sm_o[R][STATES][D];
+    __shared__ float sm_o[R][STATES][DV];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int st = wave * KPL + slot;
@@ -154,13 +162,15 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
             sm_m[r][st] = m[r];
             sm_l[r][st] = l[r];
         }
+        if (has_v) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) sm_o[r][st][t * EPL + i] = acc[r][i];
+            for (int i = 0; i < EPL; ++i) sm_o[r][st][t * EPL + i] = acc[r][i];
+        }
     }
     __syncthreads();
-    for (int idx = tid; idx < R * D; idx += kThreads) {
-        const int r = idx / D;
-        const int c = idx % D;
+    for (int idx = tid; idx < R * DV; idx += kThreads) {
+        const int r = idx / DV;
+        const int c = idx % DV;
         const int x = row0 + r;
         if (x >= G * N) continue;
         const int row = x % N;
@@ -176,9 +186,9 @@ __global__ __launch_bounds__(kThreads) void decode_segment_kernel(
                 oo = fmaf(sm_o[r][st][c], f, oo);
             }
         }
-        // Workspace layout: o_s [B*Hq, S, N, D], lse_s [B*Hq, S, N].
+        // Workspace layout: o_s [B*Hq, S, N, DV], lse_s [B*Hq, S, N].
         const int64_t part = (qhead * num_splits + split) * N + row;
-        ws_o[part * D + c] = ll > 0.f ? oo / ll : 0.f;
+        ws_o[part * DV + c] = ll > 0.f ? oo / ll : 0.f;
         if (c == 0) ws_lse[part] = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
     }
 }
@@ -297,61 +307,76 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(
     if (tid == 0) lse[hr] = total;
 }
 
-template <typename T, int D, int R>
+template <typename T, int D, int DV, int R>
 hipError_t launch_segment(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
     const int G = (int)(a.H / d.Hkv);
     const int64_t groups = ((int64_t)G * a.N + R - 1) / R;
     dim3 grid((unsigned)d.num_splits, (unsigned)(a.B * d.Hkv), (unsigned)groups);
-    hipLaunchKernelGGL((decode_segment_kernel<T, D, R>), grid, dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((decode_segment_kernel<T, D, DV, R>), grid, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), d.ws_o, d.ws_lse, (int)a.N, (int)a.Nk,
                        a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len, G);
     return hipGetLastError();
 }
 
-// Segment kernel choice.  bf16/fp16 with at least kMfmaMinRows rows per
-// key/value head (grouped heads, several queries) run on the matrix cores
-// (fa_decode_mfma.hip): there the per-key work grows with the rows and the
-// VALU kernel below would stop being bound by memory.  Otherwise the VALU
-// kernel runs with the smallest of 1, 2, 4, 8 rows per workgroup that
-// covers the rows (8 at most; more rows take more workgroups).
+// Segment kernel choice.  bf16/fp16 with d == dv <= 128 and at least
+// kMfmaMinRows rows per key/value head (grouped heads, several queries) run
+// on the matrix cores (fa_decode_mfma.hip): there the per-key work grows
+// with the rows and the VALU kernel below would stop being bound by memory.
+// Otherwise the VALU kernel runs with the smallest of 1, 2, 4, 8 rows per
+// workgroup that covers the rows (8 at most; more rows take more workgroups).
 constexpr int64_t kMfmaMinRows = 2;
 
-bool use_mfma(int dtype, int64_t rows) { return dtype != kF32 && rows >= kMfmaMinRows; }
+bool use_mfma(int dtype, int64_t d, int64_t dv, int64_t rows) {
+    return dtype != kF32 && d == dv && d <= 128 && rows >= kMfmaMinRows;
+}
 int64_t valu_rows(int64_t rows) { return rows == 1 ? 1 : rows == 2 ? 2 : rows <= 4 ? 4 : 8; }
 
-template <typename T, int D>
-hipError_t launch_dim(const DecodeArgs &d) {
+template <typename T, int D, int DV>
+hipError_t launch_dims(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
     const int64_t rows = (a.H / d.Hkv) * a.N;
     hipError_t e;
-    if (use_mfma(a.dtype, rows)) e = launch_decode_segment_mfma(d);
-    else if (valu_rows(rows) == 1) e = launch_segment<T, D, 1>(d);
-    else if (valu_rows(rows) == 2) e = launch_segment<T, D, 2>(d);
-    else if (valu_rows(rows) == 4) e = launch_segment<T, D, 4>(d);
-    else e = launch_segment<T, D, 8>(d);
+    if (use_mfma(a.dtype, a.d, a.dv, rows)) e = launch_decode_segment_mfma(d);
+    else if (valu_rows(rows) == 1) e = launch_segment<T, D, DV, 1>(d);
+    else if (valu_rows(rows) == 2) e = launch_segment<T, D, DV, 2>(d);
+    else if (valu_rows(rows) == 4) e = launch_segment<T, D, DV, 4>(d);
+    else e = launch_segment<T, D, DV, 8>(d);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(a.B * a.H * a.N)),
+    hipLaunchKernelGGL((decode_merge_kernel<T, DV>), dim3((unsigned)(a.B * a.H * a.N)),
                        dim3(kMergeWaves * 64), 0, a.stream, d.ws_o, d.ws_lse,
                        static_cast<T *>(a.o), a.lse, (int)a.N, d.num_splits);
     return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_dv(const DecodeArgs &d) {
+    switch (d.a.dv) {
+        case 32: return launch_dims<T, D, 32>(d);
+        case 64: return launch_dims<T, D, 64>(d);
+        case 128: return launch_dims<T, D, 128>(d);
+        case 256: return launch_dims<T, D, 256>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T>
 hipError_t launch_typed(const DecodeArgs &d) {
     switch (d.a.d) {
-        case 32: return launch_dim<T, 32>(d);
-        case 64: return launch_dim<T, 64>(d);
-        case 128: return launch_dim<T, 128>(d);
+        case 32: return launch_dv<T, 32>(d);
+        case 64: return launch_dv<T, 64>(d);
+        case 128: return launch_dv<T, 128>(d);
+        case 256: return launch_dv<T, 256>(d);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-int64_t decode_workgroups_per_split(int dtype, int64_t B, int64_t Hkv, int64_t rows) {
-    const int64_t per = use_mfma(dtype, rows) ? kDecodeMfmaRows : valu_rows(rows);
+int64_t decode_workgroups_per_split(int dtype, int64_t d, int64_t dv, int64_t B, int64_t Hkv,
+                                    int64_t rows) {
+    const int64_t per = use_mfma(dtype, d, dv, rows) ? kDecodeMfmaRows : valu_rows(rows);
     return B * Hkv * ((rows + per - 1) / per);
 }
 

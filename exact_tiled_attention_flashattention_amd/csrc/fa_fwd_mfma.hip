@@ -1,7 +1,8 @@
 // fa_fwd_mfma.hip -- exact attention forward on the CDNA4 matrix cores.
 //
-// bf16/fp16 inputs, d == dv == 64, scale > 0; fp32 accumulation.  (d = 128
-// runs on the variant in fa_fwd_mfma_wide.hip.)
+// bf16/fp16 inputs, (d, dv) in {(64, 64), (64, 128), (128, 64)}, scale > 0;
+// fp32 accumulation.  (d = dv = 128 runs on the variant in
+// fa_fwd_mfma_wide.hip.)
 //
 // Method: the FlashAttention-2 loop order of CS349E Lecture 11
 // "flash_lab.py", section 3 (flash_fwd, order "fa2"): one block of 256
@@ -104,24 +105,28 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
     else return 4 * (r & 7);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     T *__restrict__ o, float *__restrict__ lse, int N, int Nk, float c,
     int q_blocks, int n_items) {
     typedef typename Mfma<T>::vec vec8;
     constexpr int KS = D / 32;                  // contraction steps of S (d)
-    constexpr int DB = D / 16;                  // 16-wide value blocks of O
+    constexpr int DB = DV / 16;                 // 16-wide value blocks of O
     constexpr int KB = kBC / 16;                // 16-key blocks of S per tile
     constexpr int PC = kBC / 32;                // contraction steps of P V (keys)
-    constexpr int ROWB = D * 2;                 // bytes per key row
-    constexpr int TILE = kBC * ROWB;            // bytes per K (or V) tile
-    constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+    constexpr int ROWB = D * 2;                 // bytes per K row
+    constexpr int ROWBV = DV * 2;               // bytes per V row
+    constexpr int TILE = kBC * ROWB;            // bytes per K tile
+    constexpr int TILEV = kBC * ROWBV;          // bytes per V tile
+    constexpr int CPR = ROWB / 16;              // 16-byte chunks per K row
+    constexpr int CPRV = ROWBV / 16;            // 16-byte chunks per V row
     constexpr int NK = 3, NV = 3;               // LDS stages of K and of V
-    constexpr int LPT = TILE / 1024 / kWaves;   // 1 KiB wave loads per wave per K (or V) tile
-    static_assert(LPT * 1024 * kWaves == TILE, "tile split");
+    constexpr int LPT = TILE / 1024 / kWaves;   // 1 KiB wave loads per wave per K tile
+    constexpr int LPTV = TILEV / 1024 / kWaves; // ... per V tile
+    static_assert(LPT * 1024 * kWaves == TILE && LPTV * 1024 * kWaves == TILEV, "tile split");
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[NK][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NV][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NV][TILEV];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wave
@@ -134,13 +139,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     // rest of each address (stage, key block) is a compile-time constant.
     //  K (A operand of S^T): key row kb*16 + li, 16-byte chunk ks*4 + g.
     //  V (ds_read_b64_tr_b16): key row 4g + li/4 (+16, +32 pc), quad 4 db + li%4.
-    uint32_t kofs[D / 32], vofs[D / 16];
+    uint32_t kofs[KS], vofs[DB];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) kofs[ks] = li * (2 * D) + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
+    for (int db = 0; db < DB; ++db) {
         const int r0 = 4 * g + li / 4;
-        vofs[db] = r0 * (2 * D) + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+        vofs[db] = r0 * ROWBV + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
     }
     vec8 ones;
 #pragma unroll
@@ -213,16 +218,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     // swizzled layout is produced by choosing which global 16-byte piece each
     // lane fetches.  Rows past Nk read as zeros (buffer bounds check).
     typedef __attribute__((address_space(3))) void lds_void;
-    uint32_t koff[LPT], voff[LPT];   // per-lane global byte offsets within a tile
+    uint32_t koff[LPT], voff[LPTV];   // per-lane global byte offsets within a tile
 #pragma unroll
     for (int t = 0; t < LPT; ++t) {
         const int slot = (t * kWaves + wave) * 64 + lane;   // 16-byte slot in the tile
         const int row = slot / CPR, pc = slot % CPR;
         koff[t] = ((uint32_t)row * D + (pc ^ kswz<D>(row)) * 8) * 2u;
-        voff[t] = ((uint32_t)row * D + (((2 * pc) ^ vswz<D>(row)) / 2) * 8) * 2u;
+    }
+#pragma unroll
+    for (int t = 0; t < LPTV; ++t) {
+        const int slot = (t * kWaves + wave) * 64 + lane;
+        const int row = slot / CPRV, pc = slot % CPRV;
+        voff[t] = ((uint32_t)row * DV + (((2 * pc) ^ vswz<DV>(row)) / 2) * 8) * 2u;
     }
     const u32x4 kw = rsrc_words(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
-    const u32x4 vw = rsrc_words(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const u32x4 vw = rsrc_words(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
     const uint32_t klds = (uint32_t)(size_t)(lds_void *)&kbuf[0][0];
     const uint32_t vlds = (uint32_t)(size_t)(lds_void *)&vbuf[0][0];
     auto issue_k = [&](int j) {
@@ -236,10 +246,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     };
     auto issue_v = [&](int j) {
         if (j >= ntiles) return;
-        const uint32_t tile_off = (uint32_t)j * kBC * D * 2u;
+        const uint32_t tile_off = (uint32_t)j * kBC * DV * 2u;
 #pragma unroll
-        for (int t = 0; t < LPT; ++t) {
-            const uint32_t dst = vlds + (j % NV) * TILE + (t * kWaves + wave) * 1024;
+        for (int t = 0; t < LPTV; ++t) {
+            const uint32_t dst = vlds + (j % NV) * TILEV + (t * kWaves + wave) * 1024;
             lds_dma16(vw, __builtin_amdgcn_readfirstlane(dst), tile_off + voff[t]);
         }
     };
@@ -302,15 +312,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     // The row sums come from the matrix core too: an all-ones A operand turns
     // P^T into its column sums.
     auto accumulate = [&](auto SV) {
-        const unsigned char *base = vbuf[0] + decltype(SV)::value * TILE;
+        const unsigned char *base = vbuf[0] + decltype(SV)::value * TILEV;
         typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #pragma unroll
         for (int pc = 0; pc < PC; ++pc) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const unsigned char *p = base + pc * 32 * ROWB + vofs[db];
+                const unsigned char *p = base + pc * 32 * ROWBV + vofs[db];
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWB));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWBV));
                 const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 const vec8 a = __builtin_bit_cast(vec8, both);
                 oacc[db][0] = Mfma<T>::run(a, pb[pc][0], oacc[db][0]);
@@ -402,8 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
     auto load_step = [&](const int i) {
-        if (i + 2 < ntiles) wait_vmcnt<2 * LPT>();
-        else if (i + 1 < ntiles) wait_vmcnt<LPT>();
+        if (i + 2 < ntiles) wait_vmcnt<LPT + LPTV>();
+        else if (i + 1 < ntiles) wait_vmcnt<LPTV>();
         else wait_vmcnt<0>();
         phase_barrier();
         issue_k(i + 3);
@@ -495,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
         const int qi = qw0 + qb * 16 + li;
         if (qi >= N) continue;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        T *orow = o + ((int64_t)head * N + qi) * D;
+        T *orow = o + ((int64_t)head * N + qi) * DV;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             typedef T t4 __attribute__((ext_vector_type(4)));
@@ -511,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
 
 // Resident workgroups per CU of one kernel instantiation, times the CU count
 // of the current device (cached per device).
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int DV, bool CAUSAL>
 int resident_workgroups() {
     static int cache[64];
     int dev = 0;
@@ -522,7 +532,7 @@ int resident_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&fwd_mfma_kernel<T, D, CAUSAL>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void *>(&fwd_mfma_kernel<T, D, DV, CAUSAL>), kThreads, 0) !=
         hipSuccess)
         return 0;
     v = cus * (per_cu > 0 ? per_cu : 1);
@@ -530,37 +540,41 @@ int resident_workgroups() {
     return v;
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int DV, bool CAUSAL>
 hipError_t launch3(const FwdArgs &a) {
     const int q_blocks = (int)((a.N + kBR - 1) / kBR);
     const int64_t n_items = a.B * a.H * q_blocks;
-    const int resident = resident_workgroups<T, D, CAUSAL>();
+    const int resident = resident_workgroups<T, D, DV, CAUSAL>();
     if (resident <= 0) return hipErrorInvalidDevice;
     const int64_t grid = n_items < resident ? n_items : resident;
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, DV, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                        a.stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<T *>(a.o), a.lse, (int)a.N,
                        (int)a.Nk, a.scale * kLog2e, q_blocks, (int)n_items);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 hipError_t launch2(const FwdArgs &a) {
-    return a.causal ? launch3<T, D, true>(a) : launch3<T, D, false>(a);
+    return a.causal ? launch3<T, D, DV, true>(a) : launch3<T, D, DV, false>(a);
 }
 
 template <typename T>
 hipError_t launch1(const FwdArgs &a) {
-    return launch2<T, 64>(a);
+    if (a.d == 64 && a.dv == 64) return launch2<T, 64, 64>(a);
+    if (a.d == 64 && a.dv == 128) return launch2<T, 64, 128>(a);
+    if (a.d == 128 && a.dv == 64) return launch2<T, 128, 64>(a);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale) {
-    return (dtype == kBF16 || dtype == kF16) && d == dv && (d == 64 || d == 128) && scale > 0.f;
+    const bool dims = (d == 64 || d == 128) && (dv == 64 || dv == 128);
+    return (dtype == kBF16 || dtype == kF16) && dims && scale > 0.f;
 }
 
-hipError_t launch_fwd_mfma_d64(const FwdArgs &a) {
+hipError_t launch_fwd_mfma16(const FwdArgs &a) {
     return a.dtype == kBF16 ? launch1<bf16_t>(a) : launch1<f16_t>(a);
 }
 

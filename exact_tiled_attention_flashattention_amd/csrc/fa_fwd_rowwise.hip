@@ -1,8 +1,9 @@
 // fa_fwd_rowwise.hip -- row-parallel exact attention forward on the VALU.
 //
-// The general path of fa_fwd: every dtype, d == dv in {32, 64, 128}.  It is
-// the path for fp32 inputs, which the bf16/fp16 matrix cores cannot take
-// without losing the fp32 accuracy, and for d = 32.
+// The general path of fa_fwd: every dtype, d and dv in {32, 64, 128, 256}
+// (dv may differ from d).  It is the path for fp32 inputs, which the
+// bf16/fp16 matrix cores cannot take without losing the fp32 accuracy, and
+// for every (d, dv) the matrix-core kernels do not take.
 //
 // Method: the FlashAttention-2 loop order of CS349E Lecture 11
 // "flash_lab.py", section 3 (flash_fwd, order "fa2"): a workgroup owns a
@@ -121,23 +122,35 @@ __global__ __launch_bounds__(kThreads) void fwd_rowwise_kernel(
         lse[(int64_t)head * N + row] = l > 0.f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 hipError_t launch_typed(const FwdArgs &a) {
     const int q_blocks = (int)((a.N + kRowsPerBlock - 1) / kRowsPerBlock);
     const int64_t grid = a.B * a.H * q_blocks;
-    hipLaunchKernelGGL((fwd_rowwise_kernel<T, D, D>), dim3((unsigned)grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((fwd_rowwise_kernel<T, D, DV>), dim3((unsigned)grid), dim3(kThreads), 0,
                        a.stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<T *>(a.o), a.lse, (int)a.N,
                        (int)a.Nk, a.causal, a.scale * kLog2e, q_blocks);
     return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_dv(const FwdArgs &a) {
+    switch (a.dv) {
+        case 32: return launch_typed<T, D, 32>(a);
+        case 64: return launch_typed<T, D, 64>(a);
+        case 128: return launch_typed<T, D, 128>(a);
+        case 256: return launch_typed<T, D, 256>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T>
 hipError_t launch_dim(const FwdArgs &a) {
     switch (a.d) {
-        case 32: return launch_typed<T, 32>(a);
-        case 64: return launch_typed<T, 64>(a);
-        case 128: return launch_typed<T, 128>(a);
+        case 32: return launch_dv<T, 32>(a);
+        case 64: return launch_dv<T, 64>(a);
+        case 128: return launch_dv<T, 128>(a);
+        case 256: return launch_dv<T, 256>(a);
         default: return hipErrorInvalidValue;
     }
 }

@@ -43,12 +43,13 @@ struct BwdArgs {
     float *Dsum;          // workspace [B, H, N]: D_i = sum_c dO_ic O_ic
 };
 
-// Row-parallel VALU forward: any dtype, d == dv in {32, 64, 128}.
+// Row-parallel VALU forward: any dtype, d and dv in {32, 64, 128, 256}.
 hipError_t launch_fwd_rowwise(const FwdArgs &a);
 
-// MFMA forward for bf16/fp16 with d == dv in {64, 128} and scale > 0.
+// MFMA forward for bf16/fp16 with d, dv in {64, 128} and scale > 0:
+// d = dv = 128 on the 32x32 kernel, the other pairs on the 16x16 kernel.
 bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale);
-hipError_t launch_fwd_mfma_d64(const FwdArgs &a);    // fa_fwd_mfma.hip
+hipError_t launch_fwd_mfma16(const FwdArgs &a);      // fa_fwd_mfma.hip
 hipError_t launch_fwd_mfma_d128(const FwdArgs &a);   // fa_fwd_mfma_wide.hip
 
 // Split-KV decode: segment kernel then merge kernel, same stream.
@@ -59,7 +60,8 @@ constexpr int kDecodeMfmaRows = 16;
 hipError_t launch_decode_segment_mfma(const DecodeArgs &a);
 // Segment-kernel workgroups per split for `rows` = (Hq / Hkv) x N query rows
 // per key/value head (the same kernel choice as launch_decode_splitkv).
-int64_t decode_workgroups_per_split(int dtype, int64_t B, int64_t Hkv, int64_t rows);
+int64_t decode_workgroups_per_split(int dtype, int64_t d, int64_t dv, int64_t B, int64_t Hkv,
+                                    int64_t rows);
 
 // Backward (fa_bwd.hip): row dots, then dQ and (dK, dV); the matrix-core
 // kernels (fa_bwd_mfma.hip) take bf16/fp16 with d == dv in {64, 128}.

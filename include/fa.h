@@ -80,7 +80,10 @@ typedef enum {
  *   o, lse   outputs, layout above; o 16-byte aligned, lse 4-byte aligned.
  *   B, H     batch and head counts (>= 1).
  *   N, Nk    query rows and keys per head (>= 1).
- *   d, dv    head dims of q/k and of v/o.  Supported: d == dv in {32, 64, 128}.
+ *   d, dv    head dims of q/k and of v/o.  Supported: d and dv each in
+ *            {32, 64, 128, 256}; dv may differ from d (the pages' convention
+ *            has V [Nk, dv]).  bf16/fp16 with d == dv in {64, 128} run on the
+ *            matrix cores, every other case on the vector ALUs.
  *            Each per-head slice (N*d, Nk*d, Nk*dv, N*dv elements) must be
  *            smaller than 2 GiB, else FA_ERR_UNSUPPORTED.
  *   causal   0: no mask; non-zero: bottom-right causal mask (see above).
@@ -124,7 +127,7 @@ size_t fa_decode_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t
  *                     negative: FA_ERR_INVALID_ARG); it may exceed the key
  *                     count, surplus segments are then empty.  0 selects
  *                     fa_decode_splitkv_auto_splits(B, H, H, N, Nk, d,
- *                     dtype) segments.  Also FA_ERR_UNSUPPORTED: B*H > 65535.
+ *                     dv, dtype) segments.  Also FA_ERR_UNSUPPORTED: B*H > 65535.
  *   workspace         device scratch of at least
  *                     fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits)
  *                     bytes, 16-byte aligned, owned by the caller; its
@@ -156,7 +159,8 @@ fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void 
  *   workspace at least fa_decode_splitkv_workspace_size(B, Hq, N, dv,
  *             num_splits) bytes (partials are kept per query head).
  *   num_splits  as for fa_decode_splitkv; 0 selects
- *             fa_decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dtype).
+ *             fa_decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dv,
+ *             dtype).
  *   all else  as for fa_decode_splitkv.
  */
 fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, void *o,
@@ -174,17 +178,16 @@ fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, v
  * segment keeps at least 256 keys), and S <= 256.  The workgroup count
  * per split is B * Hkv * ceil(rows / r) with rows = (Hq / Hkv) * N and r the
  * query rows per workgroup of the kernel the shape runs on (16 for bf16 and
- * fp16 with rows >= 2; else the smallest of 1, 2, 4, 8 covering rows).
- * Pure host logic: no HIP call.
+ * fp16 with d == dv <= 128 and rows >= 2; else the smallest of 1, 2, 4, 8
+ * covering rows).  Pure host logic: no HIP call.
  *
- *   B, Hq, Hkv, N, Nk, d, dtype   as for fa_decode_splitkv_gqa (d does not
- *                                 change the current rule).
+ *   B, Hq, Hkv, N, Nk, d, dv, dtype   as for fa_decode_splitkv_gqa.
  * Returns the split count (1 .. 256), or 0 if an argument is out of range
  * (a size < 1, Hq % Hkv != 0, an unknown dtype, B * Hq or
  * (Hq / Hkv) * N above 2^31 - 1).
  */
 int fa_decode_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk,
-                                  int64_t d, fa_dtype_t dtype);
+                                  int64_t d, int64_t dv, fa_dtype_t dtype);
 
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: one

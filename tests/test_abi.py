@@ -99,8 +99,9 @@ def _dec(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=1, Nk=64, d=64, dv=64, causal=0,
     (dict(N=1 << 40), fa.FA_ERR_INVALID_ARG),
     (dict(B=1 << 32), fa.FA_ERR_INVALID_ARG),
     (dict(d=48, dv=48), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=64, dv=128), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256, dv=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64, dv=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512, dv=512), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=16, dv=64), fa.FA_ERR_UNSUPPORTED),
     (dict(Nk=1 << 22, d=128, dv=128, dtype=0), fa.FA_ERR_UNSUPPORTED),   # 2 GiB per head
     (dict(N=1 << 23, d=128, dv=128, dtype=2), fa.FA_ERR_UNSUPPORTED),    # 2 GiB per head
 ])
@@ -183,7 +184,7 @@ def test_bwd_workspace_size():
     (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(d=48, dvd=48), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=64, dvd=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64, dvd=512), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(ws=A + 4), fa.FA_ERR_WORKSPACE),
     (dict(B=2, H=3, N=5, wsb=2 * 3 * 5 * 4 - 1), fa.FA_ERR_WORKSPACE),
@@ -196,17 +197,19 @@ def test_bwd_rejects(kw, expect):
 # documented rule: the smallest power of two S with (workgroups per split) * S
 # >= 512, doubled only while Nk >= 2 S * 256, at most 256.
 @pytest.mark.parametrize("shape,expect", [
-    ((8, 32, 32, 1, 32768, 128, torch.bfloat16), 2),     # 256 workgroups per split
-    ((8, 32, 8, 1, 32768, 128, torch.bfloat16), 8),      # 4 rows in one 16-row tile: 64 per split
-    ((1, 1, 1, 1, 64, 64, torch.bfloat16), 1),           # too few keys to split
-    ((1, 1, 1, 1, 511, 64, torch.bfloat16), 1),
-    ((1, 1, 1, 1, 512, 64, torch.bfloat16), 2),          # two segments of 256
-    ((1, 1, 1, 1, 4096, 64, torch.bfloat16), 16),        # stopped by the 256-key floor
-    ((1, 1, 1, 1, 1 << 20, 64, torch.bfloat16), 256),    # the cap
+    ((8, 32, 32, 1, 32768, 128, 128, torch.bfloat16), 2),     # 256 workgroups per split
+    ((8, 32, 8, 1, 32768, 128, 128, torch.bfloat16), 8),      # 4 rows in one 16-row tile: 64 per split
+    ((1, 1, 1, 1, 64, 64, 64, torch.bfloat16), 1),           # too few keys to split
+    ((1, 1, 1, 1, 511, 64, 64, torch.bfloat16), 1),
+    ((1, 1, 1, 1, 512, 64, 64, torch.bfloat16), 2),          # two segments of 256
+    ((1, 1, 1, 1, 4096, 64, 64, torch.bfloat16), 16),        # stopped by the 256-key floor
+    ((1, 1, 1, 1, 1 << 20, 64, 64, torch.bfloat16), 256),    # the cap
     # 20 rows per key/value head: two 16-row tiles (bf16) or three 8-row groups (fp32)
-    ((12, 5, 1, 4, 1 << 20, 64, torch.bfloat16), 32),    # 24 workgroups per split
-    ((12, 5, 1, 4, 1 << 20, 64, torch.float32), 16),     # 36 workgroups per split
-    ((4, 8, 2, 1, 1 << 20, 128, torch.float16), 64),     # 4 rows, one tile: 8 per split
+    ((12, 5, 1, 4, 1 << 20, 64, 64, torch.bfloat16), 32),    # 24 workgroups per split
+    ((12, 5, 1, 4, 1 << 20, 64, 64, torch.float32), 16),     # 36 workgroups per split
+    ((4, 8, 2, 1, 1 << 20, 128, 128, torch.float16), 64),     # 4 rows, one tile: 8 per split
+    # dv != d runs on the VALU kernel (8-row groups) even for bf16: 36 per split
+    ((12, 5, 1, 4, 1 << 20, 64, 128, torch.bfloat16), 16),
 ])
 def test_auto_splits_rule(shape, expect):
     assert fa.decode_splitkv_auto_splits(*shape) == expect
@@ -214,14 +217,15 @@ def test_auto_splits_rule(shape, expect):
 
 def test_auto_splits_rejects():
     f = fa.library().fa_decode_splitkv_auto_splits
-    assert f(1, 6, 4, 1, 100, 64, 2) == 0       # Hq not a multiple of Hkv
-    assert f(1, 4, 4, 0, 100, 64, 2) == 0       # N < 1
-    assert f(1, 4, 4, 1, 0, 64, 2) == 0         # Nk < 1
-    assert f(0, 4, 4, 1, 100, 64, 2) == 0       # B < 1
-    assert f(1, 4, 4, 1, 100, 64, 3) == 0       # unknown dtype
-    assert f(1 << 20, 1 << 12, 1, 1, 100, 64, 2) == 0   # B * Hq >= 2^31
+    assert f(1, 6, 4, 1, 100, 64, 64, 2) == 0       # Hq not a multiple of Hkv
+    assert f(1, 4, 4, 0, 100, 64, 64, 2) == 0       # N < 1
+    assert f(1, 4, 4, 1, 0, 64, 64, 2) == 0         # Nk < 1
+    assert f(0, 4, 4, 1, 100, 64, 64, 2) == 0       # B < 1
+    assert f(1, 4, 4, 1, 100, 64, 0, 2) == 0        # dv < 1
+    assert f(1, 4, 4, 1, 100, 64, 64, 3) == 0       # unknown dtype
+    assert f(1 << 20, 1 << 12, 1, 1, 100, 64, 64, 2) == 0   # B * Hq >= 2^31
     with pytest.raises(ValueError):
-        fa.decode_splitkv_auto_splits(1, 6, 4, 1, 100, 64, torch.bfloat16)
+        fa.decode_splitkv_auto_splits(1, 6, 4, 1, 100, 64, 64, torch.bfloat16)
 
 
 def test_binding_requires_gpu_tensors():

@@ -180,7 +180,7 @@ def test_auto_splits_equals_explicit_count(B, Hkv, G, N, Nk, d, dtype, causal):
     """num_splits = 0 runs exactly the split count the rule reports, and the
     result is the oracle's."""
     q, k, v, o, lse = _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, 0, seed=B + G + N)
-    S = fa.decode_splitkv_auto_splits(B, Hkv * G, Hkv, N, Nk, d, q.dtype)
+    S = fa.decode_splitkv_auto_splits(B, Hkv * G, Hkv, N, Nk, d, d, q.dtype)
     assert S >= 1
     o2, l2 = fa.decode_splitkv_gqa(q, k, v, causal=causal, num_splits=S)
     torch.cuda.synchronize()
@@ -190,7 +190,7 @@ def test_auto_splits_equals_explicit_count(B, Hkv, G, N, Nk, d, dtype, causal):
 def test_auto_splits_plain_entry_point():
     q, k, v = make_inputs(2, 4, 1, 6000, 128, 128, "bf16", 9)
     o1, l1 = fa.decode_splitkv(q, k, v, num_splits=0)
-    S = fa.decode_splitkv_auto_splits(2, 4, 4, 1, 6000, 128, q.dtype)
+    S = fa.decode_splitkv_auto_splits(2, 4, 4, 1, 6000, 128, 128, q.dtype)
     o2, l2 = fa.decode_splitkv(q, k, v, num_splits=S)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
