@@ -9,8 +9,9 @@
 // recommends for decode), which turns the per-key work into small matrix
 // products: this kernel runs them on v_mfma_f32_16x16x32_{bf16,f16}.
 //
-// Mapping (one workgroup of 4 waves per (segment, key/value head, 16-row
-// tile); rows are counted over query heads x queries of the group):
+// Mapping (a persistent grid of workgroups of 4 waves, each walking units of
+// (segment, key/value head, 16-row tile); rows are counted over query heads
+// x queries of the group):
 //  * The waves take 32-key blocks of the segment round-robin; each keeps its
 //    own online-softmax state per row (section 1's rescaling rule, in base
 //    2 with the scale folded in).  A block of K and of V is fetched with
@@ -26,8 +27,10 @@
 //    {4g..4g+3, 16+4g..16+4g+3}; V^T is read from LDS with
 //    ds_read_b64_tr_b16.  Rows are XOR-swizzled in 16-byte (K) and 8-byte
 //    (V) units so that both kinds of read are free of bank conflicts.
-//  * At the end the 4 wave states of each row are merged through LDS with
-//    the same rule and written to the workspace as (o_s, lse_s).
+//  * At the end of a unit the 4 wave states of each row are merged through
+//    LDS with the same rule and written to the workspace as (o_s, lse_s).
+//    The next unit's first block and Q rows are already being fetched then,
+//    so a workgroup streams from one unit into the next without a gap.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -109,7 +112,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int N, int Nk, int causal, float c,
-    int num_splits, int seg_len, int G) {
+    int num_splits, int seg_len, int G, int heads_kv, int tiles) {
     typedef typename Mma<T>::vec vec8;
     constexpr int KS = D / 32;              // contraction steps of S^T over d
     constexpr int DB = D / 16;              // 16-column blocks of O^T
@@ -124,39 +127,47 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     __shared__ float sm_m[kWaves][kRows];
     __shared__ float sm_l[kWaves][kRows];
 
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y;             // key/value head over B x Hkv
-    const int row0 = blockIdx.z * kRows;    // first row of the tile, over G x N
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int g = lane / 16;
     const int li = lane % 16;
+    const int units = num_splits * heads_kv * tiles;
 
-    // This lane's query row: query x % N of query head kvh * G + x / N.
-    const int x = row0 + li;
-    const bool row_ok = x < G * N;
-    const int qrow = row_ok ? x % N : 0;
-    const int64_t qhead = (int64_t)kvh * G + (row_ok ? x / N : 0);
-    const int limit = !row_ok ? -1 : (causal ? Nk - N + qrow : Nk - 1);
-    vec8 qop[KS];
+    // Unit u (one segment of one key/value head for one 16-row tile) ->
+    // (split, key/value head, first row), and this wave's share of it.
+    auto unit_of = [&](int u, int &split, int &kvh, int &row0, int &seg_begin, int &seg_end,
+                       int &mine) {
+        split = u % num_splits;
+        const int rest = u / num_splits;
+        row0 = (rest % tiles) * kRows;
+        kvh = rest / tiles;
+        seg_begin = split * seg_len;
+        seg_end = min(Nk, seg_begin + seg_len);
+        const int nblk = seg_end > seg_begin ? (seg_end - seg_begin + kBlk - 1) / kBlk : 0;
+        mine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;   // blocks wave, wave+4, ...
+    };
+    // This lane's query row of a unit: query x % N of query head kvh * G + x / N.
+    auto load_q = [&](int kvh, int row0, vec8 (&qop)[KS], int &limit) {
+        const int x = row0 + li;
+        const bool row_ok = x < G * N;
+        const int qrow = row_ok ? x % N : 0;
+        const int64_t qhead = (int64_t)kvh * G + (row_ok ? x / N : 0);
+        limit = !row_ok ? -1 : (causal ? Nk - N + qrow : Nk - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (row_ok)
-            raw = *reinterpret_cast<const u32x4 *>(q + (qhead * N + qrow) * D + (ks * 4 + g) * 8);
-        qop[ks] = __builtin_bit_cast(vec8, raw);
-    }
-
-    const int seg_begin = split * seg_len;
-    const int seg_end = min(Nk, seg_begin + seg_len);
-    const int nblk = seg_end > seg_begin ? (seg_end - seg_begin + kBlk - 1) / kBlk : 0;
-    const int mine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;   // blocks wave, wave+4, ...
-
-    const T *kh = k + (int64_t)kvh * Nk * D;
-    const T *vh = v + (int64_t)kvh * Nk * D;
-    const auto krs = make_rsrc(kh, (uint32_t)Nk * D * (uint32_t)sizeof(T));
-    const auto vrs = make_rsrc(vh, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (row_ok)
+                raw = *reinterpret_cast<const u32x4 *>(q + (qhead * N + qrow) * D + (ks * 4 + g) * 8);
+            qop[ks] = __builtin_bit_cast(vec8, raw);
+        }
+    };
+    auto k_rsrc = [&](int kvh) {
+        return make_rsrc(k + (int64_t)kvh * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+    };
+    auto v_rsrc = [&](int kvh) {
+        return make_rsrc(v + (int64_t)kvh * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+    };
 
     // Per-lane byte offsets: global within a block (16-byte piece t * 64 +
     // lane of the block, row-major), LDS stores of K and V, and the LDS reads
@@ -179,16 +190,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     unsigned char *kwb = kbuf[wave];
     unsigned char *wbuf = vbuf[wave];
 
-    float m = -INFINITY, l = 0.f;
-    f32x4 oacc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The current unit.  The grid has at most `units` workgroups, so every
+    // workgroup has a first unit.
+    int u = blockIdx.x;
+    int split, kvh, row0, seg_begin, seg_end, mine, limit;
+    unit_of(u, split, kvh, row0, seg_begin, seg_end, mine);
+    vec8 qop[KS];
+    load_q(kvh, row0, qop, limit);
+    auto krs = k_rsrc(kvh), vrs = v_rsrc(kvh);
 
-    auto block_base = [&](int i) -> uint32_t {
-        return ((uint32_t)(seg_begin + (wave + kWaves * i) * kBlk) * D) * 2u;
+    float m, l;
+    f32x4 oacc[DB];
+
+    auto block_base = [&](int sb, int i) -> uint32_t {
+        return ((uint32_t)(sb + (wave + kWaves * i) * kBlk) * D) * 2u;
     };
 
-    // One 32-key block: scores, mask, online softmax, O^T += V^T P^T.
+    // One 32-key block of the current unit: scores, mask, online softmax,
+    // O^T += V^T P^T.
     auto step = [&](const u32x4 (&kr)[VL], const u32x4 (&vr)[VL], int i) {
 #pragma unroll
         for (int t = 0; t < VL; ++t) *reinterpret_cast<u32x4 *>(kwb + kw[t]) = kr[t];
@@ -242,49 +261,106 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
         }
     };
 
-    // Double-buffered loop: block i + 1's loads are in flight while block i
-    // is computed.
+    // Persistent loop over units.  Within a unit the loop is double-buffered
+    // (block i + 1's loads are in flight while block i is computed); the last
+    // block's partner load fetches the next unit's first block and its Q is
+    // loaded before the current unit's epilogue, so consecutive units stream
+    // without a gap.
     u32x4 kA[VL], vA[VL], kB[VL], vB[VL];
-    load_block<VL>(kA, vA, krs, vrs, 0 < mine, block_base(0), gofs);
-    for (int i = 0; i < mine; i += 2) {
-        load_block<VL>(kB, vB, krs, vrs, i + 1 < mine, block_base(i + 1), gofs);
-        step(kA, vA, i);
-        load_block<VL>(kA, vA, krs, vrs, i + 2 < mine, block_base(i + 2), gofs);
-        if (i + 1 < mine) step(kB, vB, i + 1);
-    }
+    load_block<VL>(kA, vA, krs, vrs, 0 < mine, block_base(seg_begin, 0), gofs);
+    for (;;) {
+        const int un = u + (int)gridDim.x;
+        const bool has_next = un < units;
+        int nsplit = 0, nkvh = kvh, nrow0 = 0, nbegin = 0, nend = 0, nmine = 0;
+        if (has_next) unit_of(un, nsplit, nkvh, nrow0, nbegin, nend, nmine);
+        const auto nkrs = k_rsrc(nkvh), nvrs = v_rsrc(nkvh);
+        const bool nfirst = has_next && nmine > 0;   // this wave has a first block of the next unit
 
-    // ---- merge the 4 wave states of each row through LDS ----------------------
-    l = rows4_sum(l);
-    float *ow = reinterpret_cast<float *>(wbuf);   // [16 rows][D], this wave's O^T
+        m = -INFINITY;
+        l = 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(ow + li * D + 16 * db + 4 * g) = oacc[db];
-    if (g == 0) {
-        sm_m[wave][li] = m;
-        sm_l[wave][li] = l;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < kRows * D; idx += kThreads) {
-        const int r = idx / D, col = idx % D;
-        const int xr = row0 + r;
-        if (xr >= G * N) continue;
-        float mm = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][r]);
-        float ll = 0.f, oo = 0.f;
-        if (mm != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float f = fast_exp2(sm_m[w][r] - mm);   // exp2(-inf) = 0
-                ll = fmaf(sm_l[w][r], f, ll);
-                oo = fmaf(reinterpret_cast<const float *>(vbuf[w])[r * D + col], f, oo);
-            }
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < mine; i += 2) {
+            load_block<VL>(kB, vB, krs, vrs, i + 1 < mine, block_base(seg_begin, i + 1), gofs);
+            step(kA, vA, i);
+            if (i + 2 < mine)
+                load_block<VL>(kA, vA, krs, vrs, true, block_base(seg_begin, i + 2), gofs);
+            else
+                load_block<VL>(kA, vA, nkrs, nvrs, nfirst, block_base(nbegin, 0), gofs);
+            if (i + 1 < mine) step(kB, vB, i + 1);
         }
-        // Workspace layout: o_s [B*Hq, S, N, D], lse_s [B*Hq, S, N].
-        const int64_t head = (int64_t)kvh * G + xr / N;
-        const int64_t part = (head * num_splits + split) * N + xr % N;
-        ws_o[part * D + col] = ll > 0.f ? oo / ll : 0.f;
-        if (col == 0) ws_lse[part] = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
+        if (mine == 0) load_block<VL>(kA, vA, nkrs, nvrs, nfirst, block_base(nbegin, 0), gofs);
+        vec8 qnext[KS];
+        int nlimit = -1;
+        if (has_next) load_q(nkvh, nrow0, qnext, nlimit);
+
+        // ---- merge the 4 wave states of each row through LDS ----------------
+        const float lt = rows4_sum(l);
+        float *ow = reinterpret_cast<float *>(wbuf);   // [16 rows][D], this wave's O^T
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(ow + li * D + 16 * db + 4 * g) = oacc[db];
+        if (g == 0) {
+            sm_m[wave][li] = m;
+            sm_l[wave][li] = lt;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < kRows * D; idx += kThreads) {
+            const int r = idx / D, col = idx % D;
+            const int xr = row0 + r;
+            if (xr >= G * N) continue;
+            float mm = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][r]);
+            float ll = 0.f, oo = 0.f;
+            if (mm != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const float f = fast_exp2(sm_m[w][r] - mm);   // exp2(-inf) = 0
+                    ll = fmaf(sm_l[w][r], f, ll);
+                    oo = fmaf(reinterpret_cast<const float *>(vbuf[w])[r * D + col], f, oo);
+                }
+            }
+            // Workspace layout: o_s [B*Hq, S, N, D], lse_s [B*Hq, S, N].
+            const int64_t head = (int64_t)kvh * G + xr / N;
+            const int64_t part = (head * num_splits + split) * N + xr % N;
+            ws_o[part * D + col] = ll > 0.f ? oo / ll : 0.f;
+            if (col == 0) ws_lse[part] = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
+        }
+        __syncthreads();   // the partials in LDS are read before the next unit overwrites them
+        if (!has_next) break;
+        u = un;
+        split = nsplit;
+        kvh = nkvh;
+        row0 = nrow0;
+        seg_begin = nbegin;
+        seg_end = nend;
+        mine = nmine;
+        limit = nlimit;
+        krs = nkrs;
+        vrs = nvrs;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = qnext[ks];
     }
+}
+
+// Resident workgroups of one instantiation on the current device (cached).
+template <typename T, int D>
+int resident_workgroups() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int val = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (val > 0) return val;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&decode_segment_mfma_kernel<T, D>), kThreads,
+            0) != hipSuccess)
+        return 0;
+    val = cus * (per_cu > 0 ? per_cu : 1);
+    __atomic_store_n(&cache[dev], val, __ATOMIC_RELAXED);
+    return val;
 }
 
 template <typename T, int D>
@@ -292,11 +368,16 @@ hipError_t launch_typed(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
     const int G = (int)(a.H / d.Hkv);
     const int64_t tiles = ((int64_t)G * a.N + kRows - 1) / kRows;
-    dim3 grid((unsigned)d.num_splits, (unsigned)(a.B * d.Hkv), (unsigned)tiles);
-    hipLaunchKernelGGL((decode_segment_mfma_kernel<T, D>), grid, dim3(kThreads), 0, a.stream,
-                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+    const int64_t units = (int64_t)d.num_splits * a.B * d.Hkv * tiles;
+    if (units > 0x7fffffff) return hipErrorInvalidValue;
+    const int resident = resident_workgroups<T, D>();
+    if (resident <= 0) return hipErrorInvalidDevice;
+    const int64_t grid = units < resident ? units : resident;
+    hipLaunchKernelGGL((decode_segment_mfma_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads),
+                       0, a.stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), d.ws_o, d.ws_lse, (int)a.N, (int)a.Nk,
-                       a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len, G);
+                       a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len, G,
+                       (int)(a.B * d.Hkv), (int)tiles);
     return hipGetLastError();
 }
 
