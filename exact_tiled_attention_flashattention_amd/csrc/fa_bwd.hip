@@ -231,12 +231,13 @@ hipError_t launch_dot(const BwdArgs &b) {
 template <typename T>
 hipError_t launch_typed(const BwdArgs &b) {
     const FwdArgs &a = b.a;
+    // The matrix-core dQ kernel computes the row dots itself.
+    if (bwd_mfma_supported(a.dtype, a.d, a.dv)) return launch_bwd_mfma(b);
     hipError_t e = a.dv == 32    ? launch_dot<T, 32>(b)
                    : a.dv == 64  ? launch_dot<T, 64>(b)
                    : a.dv == 128 ? launch_dot<T, 128>(b)
                                  : launch_dot<T, 256>(b);
     if (e != hipSuccess) return e;
-    if (bwd_mfma_supported(a.dtype, a.d, a.dv)) return launch_bwd_mfma(b);
     switch (a.d) {
         case 32: return launch_rowwise_dv<T, 32>(b);
         case 64: return launch_rowwise_dv<T, 64>(b);

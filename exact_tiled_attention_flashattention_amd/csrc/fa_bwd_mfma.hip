@@ -4,7 +4,8 @@
 // Method: CS349E Lecture 11 "flash_lab.py", section 5 (flash_bwd, the
 // FlashAttention-2 backward).  The probabilities are recomputed from Q, K
 // and the forward's LSE, P = exp(S - LSE) (here exp2 of S scale log2(e) -
-// LSE log2(e)); with D_i = rowsum(dO o O) (the row-dot kernel of fa_bwd.hip):
+// LSE log2(e)); with D_i = rowsum(dO o O) (computed by the dQ kernel, which
+// runs first, from the dO rows it holds anyway):
 //     dV += P^T dO,  dP = dO V^T,  dS = P o (dP - D),
 //     dK += dS^T Q (times scale),  dQ += dS K (times scale).
 // As in fa_bwd.hip the two halves run as separate kernels (no location is
@@ -101,6 +102,14 @@ __device__ __forceinline__ void work_item(int nblk, int heads, int &head, int &b
         head = L / nblk;
         blk = L % nblk;
     }
+}
+
+// Sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows4_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(a[0]) + __int_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
 template <typename T>
@@ -354,8 +363,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
-    T *__restrict__ dq, int N, int Nk, float c, float scale, int heads) {
+    const float *__restrict__ lse, const T *__restrict__ dout, const T *__restrict__ o,
+    float *__restrict__ Dsum, T *__restrict__ dq, int N, int Nk, float c, float scale, int heads) {
     typedef typename Mma<T>::vec vec8;
     constexpr int KS = D / 32;
     constexpr int DB = D / 16;
@@ -386,18 +395,27 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
     const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
     const auto vrs = make_rsrc(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
 
+    // Q^T and dO^T B operands, and this row's D = sum_c dO_c O_c from the same
+    // column slices of O (summed over the four lane groups); D is also written
+    // for the dK/dV kernel, which runs after this one.
+    const auto ors = make_rsrc(o + (int64_t)head * N * D, (uint32_t)N * D * 2u);
     vec8 qop[KS], dop[KS];
+    float dpart = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const uint32_t off = ((uint32_t)row * D + ks * 32 + 8 * g) * 2u;
         qop[ks] = as_vec<T>(buffer_load16(qrs, off));
         dop[ks] = as_vec<T>(buffer_load16(drs, off));
+        const vec8 ov = as_vec<T>(buffer_load16(ors, off));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dpart = fmaf(to_f32(ov[j]), to_f32(dop[ks][j]), dpart);
     }
-    float lse2 = INFINITY, Drow = 0.f;
+    const float Drow = rows4_sum(dpart);
+    float lse2 = INFINITY;
     if (row < N) {
         const float L = lse[(int64_t)head * N + row];
         lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
-        Drow = Dsum[(int64_t)head * N + row];
+        if (g == 0) Dsum[(int64_t)head * N + row] = Drow;
     }
 
     const int off_c = Nk - N;
@@ -533,20 +551,21 @@ hipError_t launch3(const BwdArgs &b) {
     const FwdArgs &a = b.a;
     const unsigned heads = (unsigned)(a.B * a.H);
     const float c = a.scale * kLog2e;
+    // dQ first: it also writes the row dots D that the dK/dV kernel reads.
+    const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAUSAL>), gq, dim3(kThreads), 0, a.stream,
+                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                       static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
+                       static_cast<const T *>(a.o), b.Dsum, static_cast<T *>(b.dq), (int)a.N,
+                       (int)a.Nk, c, a.scale, (int)heads);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAUSAL>), gk, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        b.Dsum, static_cast<T *>(b.dk), static_cast<T *>(b.dv), (int)a.N,
                        (int)a.Nk, c, a.scale, (int)heads);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAUSAL>), gq, dim3(kThreads), 0, a.stream,
-                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
-                       static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
-                       b.Dsum, static_cast<T *>(b.dq), (int)a.N, (int)a.Nk, c, a.scale,
-                       (int)heads);
     return hipGetLastError();
 }
 
