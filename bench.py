@@ -409,7 +409,7 @@ def bench_bwd(args, torch, fa, si, dev) -> int:
         "data": "synthetic (seeded torch Philox draws on the GPU)",
         "config": {"workload": PREFILL + " (fa_bwd)", "B": s.B, "H": s.H, "N": s.N, "Nk": s.Nk,
                    "d": s.d, "causal": True},
-        "roofline": {"kernel": "bwd_dkdv_mfma_kernel + bwd_dq_mfma_kernel (+ bwd_dot_kernel)",
+        "roofline": {"kernel": "bwd_dq_mfma_kernel + bwd_dkdv_mfma_kernel",
                      "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "avg_launch_us": round(avg_s * 1e6, 2), "min_launch_us": round(min(ms) * 1e3, 2),
