@@ -19,7 +19,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd_rowwise.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma_wide.hip", "fa_decode.hip",
-           "fa_decode_mfma.hip", "fa_bwd.hip", "fa_bwd_mfma.hip"]
+           "fa_decode_mfma.hip", "fa_bwd.hip", "fa_bwd_mfma.hip",
+           "fa_fwd_mfma_generic.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

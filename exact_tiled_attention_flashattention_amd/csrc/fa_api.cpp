@@ -129,9 +129,12 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, void *o, float *
     if (st != FA_OK) return st;
     fa::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, Nk, d, dv, causal, scale, dtype, stream);
     (void)hipGetLastError();   // clear any stale error so it is not reported as ours
-    hipError_t e = !fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_rowwise(a)
-                   : (d == 128 && dv == 128)                    ? fa::launch_fwd_mfma_d128(a)
-                                                                : fa::launch_fwd_mfma16(a);
+    // fp32: the VALU kernel (the 2e-5 bar needs fp32 operands); bf16/fp16:
+    // the tuned matrix-core kernels where they apply, else the generic one.
+    hipError_t e = dtype == FA_DTYPE_F32                         ? fa::launch_fwd_rowwise(a)
+                   : !fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_mfma_generic(a)
+                   : (d == 128 && dv == 128)                       ? fa::launch_fwd_mfma_d128(a)
+                                                                   : fa::launch_fwd_mfma16(a);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -51,6 +51,9 @@ hipError_t launch_fwd_rowwise(const FwdArgs &a);
 bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale);
 hipError_t launch_fwd_mfma16(const FwdArgs &a);      // fa_fwd_mfma.hip
 hipError_t launch_fwd_mfma_d128(const FwdArgs &a);   // fa_fwd_mfma_wide.hip
+// MFMA forward for every other bf16/fp16 case (any d, dv of 32..256, any
+// scale), fa_fwd_mfma_generic.hip.
+hipError_t launch_fwd_mfma_generic(const FwdArgs &a);
 
 // Split-KV decode: segment kernel then merge kernel, same stream.
 hipError_t launch_decode_splitkv(const DecodeArgs &a);

@@ -82,8 +82,9 @@ typedef enum {
  *   N, Nk    query rows and keys per head (>= 1).
  *   d, dv    head dims of q/k and of v/o.  Supported: d and dv each in
  *            {32, 64, 128, 256}; dv may differ from d (the pages' convention
- *            has V [Nk, dv]).  bf16/fp16 with d == dv in {64, 128} run on the
- *            matrix cores, every other case on the vector ALUs.
+ *            has V [Nk, dv]).  bf16/fp16 run on the matrix cores (tuned
+ *            kernels for d, dv in {64, 128} with scale > 0, a generic one
+ *            otherwise); fp32 runs on the vector ALUs.
  *            Each per-head slice (N*d, Nk*d, Nk*dv, N*dv elements) must be
  *            smaller than 2 GiB, else FA_ERR_UNSUPPORTED.
  *   causal   0: no mask; non-zero: bottom-right causal mask (see above).
