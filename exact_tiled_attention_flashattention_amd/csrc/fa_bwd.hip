@@ -15,9 +15,8 @@
 // location is written by more than one workgroup and the result is
 // deterministic.  The price is that S, P and dP are recomputed in both.
 //
-// The VALU kernels here serve fp32 (whose 2e-5 bar needs fp32 operands) and
-// every (d, dv) the matrix-core kernels do not take (d, dv in {32, 64, 128,
-// 256}, dv may differ from d): one wave per query row
+// The VALU kernels here serve fp32, whose 2e-5 bar needs fp32 operands (the
+// matrix-core kernels take every bf16/fp16 (d, dv)): one wave per query row
 // (dQ) or per key (dK, dV), the head dimension spread over the lanes, dot
 // products summed over the wave.
 #include "fa_device.h"

@@ -1,5 +1,5 @@
 // fa_bwd_mfma.hip -- attention backward on the CDNA4 matrix cores
-// (bf16/fp16 inputs, d == dv in {64, 128}, fp32 accumulation).
+// (bf16/fp16 inputs, d and dv in {32, 64, 128, 256}, fp32 accumulation).
 //
 // Method: CS349E Lecture 11 "flash_lab.py", section 5 (flash_bwd, the
 // FlashAttention-2 backward).  The probabilities are recomputed from Q, K
@@ -81,10 +81,12 @@ constexpr int kThreads = kWaves * 64;
 template <int D> __device__ __forceinline__ int kswz(int r) {
     if constexpr (D == 64)
         return ((r >> 2) & 1) | ((__builtin_popcount(r & 15) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+    else if constexpr (D == 32) return r & 3;
     else return r & 15;
 }
 template <int D> __device__ __forceinline__ int vswz(int r) {
     if constexpr (D == 64) return 4 * ((r & 3) ^ ((r >> 2) & 1));
+    else if constexpr (D == 32) return 0;
     else return 4 * (r & 7);
 }
 
@@ -145,27 +147,33 @@ __device__ __forceinline__ typename Mma<T>::vec pack_b(f32x4 a, f32x4 b) {
     return r;
 }
 
+// Waves per SIMD the launch bounds ask for: 4 (two resident workgroups per
+// CU, at most 128 registers) for the small head dimensions, 2 otherwise.
+template <int D, int DV> constexpr int bwd_waves_per_simd() { return D + DV <= 128 ? 4 : 2; }
+
 // =============================================================================
 // dK, dV
 // =============================================================================
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kernel(
+template <typename T, int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_dkdv_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
     T *__restrict__ dk, T *__restrict__ dvo, int N, int Nk, float c, float scale, int heads) {
     typedef typename Mma<T>::vec vec8;
-    constexpr int KS = D / 32;              // contraction steps over d
-    constexpr int DB = D / 16;              // 16-column blocks of dK^T / dV^T
-    constexpr int ROWB = 2 * D;             // bytes per row
-    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+    constexpr int KS = D / 32;              // contraction steps of S = Q K^T (over d)
+    constexpr int KSV = DV / 32;            // contraction steps of dP = dO V^T (over dv)
+    constexpr int DBK = D / 16;             // 16-column blocks of dK^T
+    constexpr int DBV = DV / 16;            // 16-column blocks of dV^T
+    constexpr int ROWQ = 2 * D, ROWO = 2 * DV;   // bytes per Q / dO row
+    constexpr int CPRQ = ROWQ / 16, CPRO = ROWO / 16;
     constexpr int QS = 32;                  // query rows per step
-    constexpr int TILE = QS * ROWB;         // bytes of one 32-row copy
-    constexpr int CH = QS * CPR;            // chunks of one tensor per step
-    constexpr int NL = 2 * CH / kThreads;   // chunks per thread per step (Q and dO)
-    static_assert(NL >= 1 && NL * kThreads == 2 * CH, "load split");
+    constexpr int TQ = QS * ROWQ, TO = QS * ROWO;   // bytes of one copy of a step's Q / dO
+    constexpr int CHQ = QS * CPRQ, CHO = QS * CPRO; // 16-byte chunks of Q / dO per step
+    constexpr int NL = (CHQ + CHO + kThreads - 1) / kThreads;   // chunks per thread per step
 
     // Per stage: Q row-major, Q transposing, dO row-major, dO transposing.
-    __shared__ __attribute__((aligned(16))) unsigned char buf[2][4][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char bq[2][2][TQ];
+    __shared__ __attribute__((aligned(16))) unsigned char bo[2][2][TO];
     __shared__ float s_lse[2][QS];
     __shared__ float s_D[2][QS];
 
@@ -181,22 +189,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
     const int key = kw0 + li;               // this lane's key (MFMA column)
 
     const T *qh = q + (int64_t)head * N * D;
-    const T *dh = dout + (int64_t)head * N * D;
+    const T *dh = dout + (int64_t)head * N * DV;
     const float *Lh = lse + (int64_t)head * N;
     const float *Dh = Dsum + (int64_t)head * N;
     const auto qrs = make_rsrc(qh, (uint32_t)N * D * 2u);
-    const auto drs = make_rsrc(dh, (uint32_t)N * D * 2u);
+    const auto drs = make_rsrc(dh, (uint32_t)N * DV * 2u);
     const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
-    const auto vrs = make_rsrc(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const auto vrs = make_rsrc(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
 
-    // K^T and V^T B operands: lane holds row `key`, columns 32 ks + 8g .. +7.
-    vec8 kop[KS], vop[KS];
+    // K^T and V^T B operands: lane holds the row of `key`, columns 32 ks + 8g .. +7.
+    vec8 kop[KS], vop[KSV];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t off = ((uint32_t)key * D + ks * 32 + 8 * g) * 2u;
-        kop[ks] = as_vec<T>(buffer_load16(krs, off));
-        vop[ks] = as_vec<T>(buffer_load16(vrs, off));
-    }
+    for (int ks = 0; ks < KS; ++ks)
+        kop[ks] = as_vec<T>(buffer_load16(krs, ((uint32_t)key * D + ks * 32 + 8 * g) * 2u));
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks)
+        vop[ks] = as_vec<T>(buffer_load16(vrs, ((uint32_t)key * DV + ks * 32 + 8 * g) * 2u));
 
     // Steps over query rows: all rows, or (causal) from the first row that
     // sees key j0.
@@ -207,36 +215,58 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
 
     // Per-thread load slots: chunk t * kThreads + tid of [Q chunks | dO chunks].
     uint32_t gofs[NL], wA[NL], wT[NL];
-    bool isdo[NL];
+    bool isdo[NL], used[NL];
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
         const int cidx = t * kThreads + tid;
-        isdo[t] = cidx >= CH;
-        const int ch = cidx % CH;
-        const int row = ch / CPR, cc = ch % CPR;
-        gofs[t] = ((uint32_t)row * D + cc * 8) * 2u;
-        wA[t] = row * ROWB + ((cc ^ kswz<D>(row)) * 16);
-        wT[t] = row * ROWB + (((2 * cc) ^ vswz<D>(row)) * 8);
+        used[t] = (CHQ + CHO) % kThreads == 0 || cidx < CHQ + CHO;
+        isdo[t] = cidx >= CHQ;
+        if constexpr (D == DV) {   // one layout for both tensors
+            const int ch = cidx % CHQ;
+            const int row = ch / CPRQ, cc = ch % CPRQ;
+            gofs[t] = ((uint32_t)row * D + cc * 8) * 2u;
+            wA[t] = row * ROWQ + ((cc ^ kswz<D>(row)) * 16);
+            wT[t] = row * ROWQ + (((2 * cc) ^ vswz<D>(row)) * 8);
+            continue;
+        }
+        gofs[t] = wA[t] = wT[t] = 0;
+        if (!used[t]) continue;
+        if (!isdo[t]) {
+            const int row = cidx / CPRQ, cc = cidx % CPRQ;
+            gofs[t] = ((uint32_t)row * D + cc * 8) * 2u;
+            wA[t] = row * ROWQ + ((cc ^ kswz<D>(row)) * 16);
+            wT[t] = row * ROWQ + (((2 * cc) ^ vswz<D>(row)) * 8);
+        } else {
+            const int ch = cidx - CHQ;
+            const int row = ch / CPRO, cc = ch % CPRO;
+            gofs[t] = ((uint32_t)row * DV + cc * 8) * 2u;
+            wA[t] = row * ROWO + ((cc ^ kswz<DV>(row)) * 16);
+            wT[t] = row * ROWO + (((2 * cc) ^ vswz<DV>(row)) * 8);
+        }
     }
     // Per-lane read offsets.
-    uint32_t rA[KS], rT[DB];
+    uint32_t rAq[KS], rAo[KSV], rTq[DBK], rTo[DBV];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) rA[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+    for (int ks = 0; ks < KS; ++ks) rAq[ks] = li * ROWQ + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const int r0 = 4 * g + li / 4;
-        rT[db] = r0 * ROWB + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
-    }
+    for (int ks = 0; ks < KSV; ++ks) rAo[ks] = li * ROWO + (((ks * 4 + g) ^ kswz<DV>(li)) * 16);
+    const int r0 = 4 * g + li / 4;
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) rTq[db] = r0 * ROWQ + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+#pragma unroll
+    for (int db = 0; db < DBV; ++db) rTo[db] = r0 * ROWO + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
 
     // Steps are fetched two ahead: step x's data waits in register set x % 2
     // until it is stored to LDS stage x % 2 at the end of step x - 1.
     u32x4 regs0[NL], regs1[NL];
     float val0 = 0.f, val1 = 0.f;
     auto load_step = [&](u32x4 (&rg)[NL], float &val, int s) {   // global -> registers
-        const uint32_t base = (uint32_t)((s0 + s) * QS) * D * 2u;
+        const uint32_t baseq = (uint32_t)((s0 + s) * QS) * D * 2u;
+        const uint32_t baseo = (uint32_t)((s0 + s) * QS) * DV * 2u;
 #pragma unroll
         for (int t = 0; t < NL; ++t)
-            rg[t] = isdo[t] ? buffer_load16(drs, base + gofs[t]) : buffer_load16(qrs, base + gofs[t]);
+            if (used[t])
+                rg[t] = isdo[t] ? buffer_load16(drs, baseo + gofs[t]) : buffer_load16(qrs, baseq + gofs[t]);
         if (tid < 2 * QS) {
             const int row = (s0 + s) * QS + (tid % QS);
             if (tid < QS) {
@@ -250,8 +280,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
     auto store_step = [&](const u32x4 (&rg)[NL], float val, int st) {   // registers -> LDS
 #pragma unroll
         for (int t = 0; t < NL; ++t) {
-            unsigned char *a = buf[st][isdo[t] ? 2 : 0];
-            unsigned char *b = buf[st][isdo[t] ? 3 : 1];
+            if (!used[t]) continue;
+            unsigned char *a = isdo[t] ? bo[st][0] : bq[st][0];
+            unsigned char *b = isdo[t] ? bo[st][1] : bq[st][1];
             *reinterpret_cast<u32x4 *>(a + wA[t]) = rg[t];
             *reinterpret_cast<u32x4 *>(b + wT[t]) = rg[t];
         }
@@ -259,29 +290,37 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
         else if (tid < 2 * QS) s_D[st][tid - QS] = val;
     };
 
-    f32x4 dka[DB], dva[DB];
+    f32x4 dka[DBK], dva[DBV];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        dka[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dva[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int db = 0; db < DBK; ++db) dka[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < DBV; ++db) dva[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int s, int st) {
         const int i0 = (s0 + s) * QS;
         // Skip when no row of this step sees any of the wave's keys.
         const bool active = !CAUSAL || kw0 <= off_c + i0 + QS - 1;
         if (active) {
-            const unsigned char *qa = buf[st][0], *qt = buf[st][1];
-            const unsigned char *da = buf[st][2], *dt = buf[st][3];
+            const unsigned char *qa = bq[st][0], *qt = bq[st][1];
+            const unsigned char *da = bo[st][0], *dt = bo[st][1];
             f32x4 S[2], dP[2];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 S[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dP[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (D == DV) {   // the two products interleaved step by step
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWB + rA[ks])), kop[ks], S[rb]);
-                    dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWB + rA[ks])), vop[ks], dP[rb]);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWQ + rAq[ks])), kop[ks], S[rb]);
+                        dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWO + rAq[ks])), vop[ks], dP[rb]);
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWQ + rAq[ks])), kop[ks], S[rb]);
+#pragma unroll
+                    for (int ks = 0; ks < KSV; ++ks)
+                        dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWO + rAo[ks])), vop[ks], dP[rb]);
                 }
             }
             // P and dS of rows rb*16 + 4g + r, key `key`.  Only steps where
@@ -312,10 +351,19 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
             }
             const vec8 pb = pack_b<T>(S[0], S[1]);
             const vec8 sb = pack_b<T>(dP[0], dP[1]);
+            if constexpr (D == DV) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dva[db] = Mma<T>::run(lds_tr32<T, ROWB>(dt + rT[db]), pb, dva[db]);
-                dka[db] = Mma<T>::run(lds_tr32<T, ROWB>(qt + rT[db]), sb, dka[db]);
+                for (int db = 0; db < DBK; ++db) {
+                    dva[db] = Mma<T>::run(lds_tr32<T, ROWO>(dt + rTq[db]), pb, dva[db]);
+                    dka[db] = Mma<T>::run(lds_tr32<T, ROWQ>(qt + rTq[db]), sb, dka[db]);
+                }
+            } else {
+#pragma unroll
+                for (int db = 0; db < DBV; ++db)
+                    dva[db] = Mma<T>::run(lds_tr32<T, ROWO>(dt + rTo[db]), pb, dva[db]);
+#pragma unroll
+                for (int db = 0; db < DBK; ++db)
+                    dka[db] = Mma<T>::run(lds_tr32<T, ROWQ>(qt + rTq[db]), sb, dka[db]);
             }
         }
     };
@@ -340,18 +388,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
 
     // dK^T, dV^T result blocks: lane holds columns 16 db + 4g + r of `key`.
     if (key < Nk) {
+        typedef T t4 __attribute__((ext_vector_type(4)));
         T *dkr = dk + ((int64_t)head * Nk + key) * D;
-        T *dvr = dvo + ((int64_t)head * Nk + key) * D;
+        T *dvr = dvo + ((int64_t)head * Nk + key) * DV;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            typedef T t4 __attribute__((ext_vector_type(4)));
-            t4 a, b;
+        for (int db = 0; db < DBK; ++db) {
+            t4 a;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                a[r] = static_cast<T>(dka[db][r] * scale);
-                b[r] = static_cast<T>(dva[db][r]);
-            }
+            for (int r = 0; r < 4; ++r) a[r] = static_cast<T>(dka[db][r] * scale);
             *reinterpret_cast<t4 *>(dkr + 16 * db + 4 * g) = a;
+        }
+#pragma unroll
+        for (int db = 0; db < DBV; ++db) {
+            t4 b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[r] = static_cast<T>(dva[db][r]);
             *reinterpret_cast<t4 *>(dvr + 16 * db + 4 * g) = b;
         }
     }
@@ -360,24 +411,27 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dkdv_mfma_kerne
 // =============================================================================
 // dQ
 // =============================================================================
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
+template <typename T, int D, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_dq_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const T *__restrict__ o,
     float *__restrict__ Dsum, T *__restrict__ dq, int N, int Nk, float c, float scale, int heads) {
     typedef typename Mma<T>::vec vec8;
-    constexpr int KS = D / 32;
-    constexpr int DB = D / 16;
-    constexpr int ROWB = 2 * D;
-    constexpr int CPR = ROWB / 16;
-    constexpr int BC = 64;                  // keys per step
-    constexpr int TILE = BC * ROWB;
-    constexpr int CH = BC * CPR;            // chunks of one tensor per step
-    constexpr int NL = 2 * CH / kThreads;   // chunks per thread per step (K and V)
-    static_assert(NL >= 1 && NL * kThreads == 2 * CH, "load split");
+    constexpr int KS = D / 32;              // contraction steps of S^T = K Q^T (over d)
+    constexpr int KSV = DV / 32;            // contraction steps of dP^T = V dO^T (over dv)
+    constexpr int DB = D / 16;              // 16-column blocks of dQ^T
+    constexpr int ROWK = 2 * D, ROWV = 2 * DV;   // bytes per K / V row
+    constexpr int CPRK = ROWK / 16, CPRV = ROWV / 16;
+    constexpr int BC = D + DV <= 256 ? 64 : 32;     // keys per step (LDS: 2 stages of 3 copies)
+    constexpr int KB = BC / 16;             // 16-key score blocks per step
+    constexpr int PC = BC / 32;             // 32-key contraction steps of dQ^T
+    constexpr int TK = BC * ROWK, TV = BC * ROWV;
+    constexpr int CHK = BC * CPRK, CHV = BC * CPRV;
+    constexpr int NL = (CHK + CHV + kThreads - 1) / kThreads;   // chunks per thread per step
 
     // Per stage: K row-major, K transposing, V row-major.
-    __shared__ __attribute__((aligned(16))) unsigned char buf[2][3][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char bk[2][2][TK];
+    __shared__ __attribute__((aligned(16))) unsigned char bv[2][TV];
 
     int head, qblk;
     work_item((N + kWaves * 16 - 1) / (kWaves * 16), heads, head, qblk);
@@ -391,24 +445,29 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
     const int row = qw0 + li;               // this lane's query row (MFMA column)
 
     const auto qrs = make_rsrc(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
-    const auto drs = make_rsrc(dout + (int64_t)head * N * D, (uint32_t)N * D * 2u);
+    const auto drs = make_rsrc(dout + (int64_t)head * N * DV, (uint32_t)N * DV * 2u);
+    const auto ors = make_rsrc(o + (int64_t)head * N * DV, (uint32_t)N * DV * 2u);
     const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
-    const auto vrs = make_rsrc(v + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    const auto vrs = make_rsrc(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
 
     // Q^T and dO^T B operands, and this row's D = sum_c dO_c O_c from the same
     // column slices of O (summed over the four lane groups); D is also written
     // for the dK/dV kernel, which runs after this one.
-    const auto ors = make_rsrc(o + (int64_t)head * N * D, (uint32_t)N * D * 2u);
-    vec8 qop[KS], dop[KS];
+    vec8 qop[KS], dop[KSV];
     float dpart = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t off = ((uint32_t)row * D + ks * 32 + 8 * g) * 2u;
-        qop[ks] = as_vec<T>(buffer_load16(qrs, off));
+    for (int ks = 0; ks < KSV; ++ks) {
+        const uint32_t off = ((uint32_t)row * DV + ks * 32 + 8 * g) * 2u;
+        if (D == DV) qop[ks] = as_vec<T>(buffer_load16(qrs, off));
         dop[ks] = as_vec<T>(buffer_load16(drs, off));
         const vec8 ov = as_vec<T>(buffer_load16(ors, off));
 #pragma unroll
         for (int j = 0; j < 8; ++j) dpart = fmaf(to_f32(ov[j]), to_f32(dop[ks][j]), dpart);
+    }
+    if (D != DV) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qop[ks] = as_vec<T>(buffer_load16(qrs, ((uint32_t)row * D + ks * 32 + 8 * g) * 2u));
     }
     const float Drow = rows4_sum(dpart);
     float lse2 = INFINITY;
@@ -423,41 +482,63 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
     const int nsteps = key_end > 0 ? (key_end + BC - 1) / BC : 0;
 
     uint32_t gofs[NL], wA[NL], wT[NL];
-    bool isv[NL];
+    bool isv[NL], used[NL];
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
         const int cidx = t * kThreads + tid;
-        isv[t] = cidx >= CH;
-        const int ch = cidx % CH;
-        const int r = ch / CPR, cc = ch % CPR;
-        gofs[t] = ((uint32_t)r * D + cc * 8) * 2u;
-        wA[t] = r * ROWB + ((cc ^ kswz<D>(r)) * 16);
-        wT[t] = r * ROWB + (((2 * cc) ^ vswz<D>(r)) * 8);
+        used[t] = (CHK + CHV) % kThreads == 0 || cidx < CHK + CHV;
+        isv[t] = cidx >= CHK;
+        if constexpr (D == DV) {   // one layout for both tensors
+            const int ch = cidx % CHK;
+            const int r = ch / CPRK, cc = ch % CPRK;
+            gofs[t] = ((uint32_t)r * D + cc * 8) * 2u;
+            wA[t] = r * ROWK + ((cc ^ kswz<D>(r)) * 16);
+            wT[t] = r * ROWK + (((2 * cc) ^ vswz<D>(r)) * 8);
+            continue;
+        }
+        gofs[t] = wA[t] = wT[t] = 0;
+        if (!used[t]) continue;
+        if (!isv[t]) {
+            const int r = cidx / CPRK, cc = cidx % CPRK;
+            gofs[t] = ((uint32_t)r * D + cc * 8) * 2u;
+            wA[t] = r * ROWK + ((cc ^ kswz<D>(r)) * 16);
+            wT[t] = r * ROWK + (((2 * cc) ^ vswz<D>(r)) * 8);
+        } else {
+            const int ch = cidx - CHK;
+            const int r = ch / CPRV, cc = ch % CPRV;
+            gofs[t] = ((uint32_t)r * DV + cc * 8) * 2u;
+            wA[t] = r * ROWV + ((cc ^ kswz<DV>(r)) * 16);
+        }
     }
-    uint32_t rA[KS], rT[DB];
+    uint32_t rAk[KS], rAv[KSV], rT[DB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) rA[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+    for (int ks = 0; ks < KS; ++ks) rAk[ks] = li * ROWK + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks) rAv[ks] = li * ROWV + (((ks * 4 + g) ^ kswz<DV>(li)) * 16);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         const int r0 = 4 * g + li / 4;
-        rT[db] = r0 * ROWB + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+        rT[db] = r0 * ROWK + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
     }
 
     u32x4 regs0[NL], regs1[NL];
     auto load_step = [&](u32x4 (&rg)[NL], int s) {
-        const uint32_t base = (uint32_t)(s * BC) * D * 2u;
+        const uint32_t basek = (uint32_t)(s * BC) * D * 2u;
+        const uint32_t basev = D == DV ? basek : (uint32_t)(s * BC) * DV * 2u;
 #pragma unroll
         for (int t = 0; t < NL; ++t)
-            rg[t] = isv[t] ? buffer_load16(vrs, base + gofs[t]) : buffer_load16(krs, base + gofs[t]);
+            if (used[t])
+                rg[t] = isv[t] ? buffer_load16(vrs, basev + gofs[t]) : buffer_load16(krs, basek + gofs[t]);
     };
     auto store_step = [&](const u32x4 (&rg)[NL], int st) {
 #pragma unroll
         for (int t = 0; t < NL; ++t) {
+            if (!used[t]) continue;
             if (isv[t]) {
-                *reinterpret_cast<u32x4 *>(buf[st][2] + wA[t]) = rg[t];
+                *reinterpret_cast<u32x4 *>(bv[st] + wA[t]) = rg[t];
             } else {
-                *reinterpret_cast<u32x4 *>(buf[st][0] + wA[t]) = rg[t];
-                *reinterpret_cast<u32x4 *>(buf[st][1] + wT[t]) = rg[t];
+                *reinterpret_cast<u32x4 *>(bk[st][0] + wA[t]) = rg[t];
+                *reinterpret_cast<u32x4 *>(bk[st][1] + wT[t]) = rg[t];
             }
         }
     };
@@ -470,16 +551,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
         const int j0 = s * BC;
         const bool active = qw0 < N && (!CAUSAL || j0 <= off_c + qw0 + 15);
         if (active) {
-            const unsigned char *ka = buf[st][0], *kt = buf[st][1], *va = buf[st][2];
-            f32x4 S[4], dP[4];
+            const unsigned char *ka = bk[st][0], *kt = bk[st][1], *va = bv[st];
+            f32x4 S[KB], dP[KB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dP[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if constexpr (D == DV) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    S[kb] = Mma<T>::run(as_vec<T>(lds_row16(ka + kb * 16 * ROWB + rA[ks])), qop[ks], S[kb]);
-                    dP[kb] = Mma<T>::run(as_vec<T>(lds_row16(va + kb * 16 * ROWB + rA[ks])), dop[ks], dP[kb]);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        S[kb] = Mma<T>::run(as_vec<T>(lds_row16(ka + kb * 16 * ROWK + rAk[ks])), qop[ks], S[kb]);
+                        dP[kb] = Mma<T>::run(as_vec<T>(lds_row16(va + kb * 16 * ROWV + rAk[ks])), dop[ks], dP[kb]);
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        S[kb] = Mma<T>::run(as_vec<T>(lds_row16(ka + kb * 16 * ROWK + rAk[ks])), qop[ks], S[kb]);
+#pragma unroll
+                    for (int ks = 0; ks < KSV; ++ks)
+                        dP[kb] = Mma<T>::run(as_vec<T>(lds_row16(va + kb * 16 * ROWV + rAv[ks])), dop[ks], dP[kb]);
                 }
             }
             // As in the dK/dV kernel, only steps that reach past some row's
@@ -487,17 +577,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
             const bool masked = j0 + BC > Nk || (CAUSAL && j0 + BC - 1 > off_c + qw0);
             if (masked) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int key = j0 + kb * 16 + 4 * g + r;
-                        const bool vis = key < Nk && (!CAUSAL || key <= off_c + row);
+                        const int kk = j0 + kb * 16 + 4 * g + r;
+                        const bool vis = kk < Nk && (!CAUSAL || kk <= off_c + row);
                         const float p = vis ? fast_exp2(fmaf(S[kb][r], c, -lse2)) : 0.f;
                         dP[kb][r] = p * (dP[kb][r] - Drow);
                     }
             } else {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float p = fast_exp2(fmaf(S[kb][r], c, -lse2));
@@ -505,11 +595,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
                     }
             }
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc) {
+            for (int pc = 0; pc < PC; ++pc) {
                 const vec8 sb = pack_b<T>(dP[2 * pc], dP[2 * pc + 1]);
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    dqa[db] = Mma<T>::run(lds_tr32<T, ROWB>(kt + pc * 32 * ROWB + rT[db]), sb, dqa[db]);
+                    dqa[db] = Mma<T>::run(lds_tr32<T, ROWK>(kt + pc * 32 * ROWK + rT[db]), sb, dqa[db]);
             }
         }
     };
@@ -546,14 +636,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void bwd_dq_mfma_kernel(
     }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int DV, bool CAUSAL>
 hipError_t launch3(const BwdArgs &b) {
     const FwdArgs &a = b.a;
     const unsigned heads = (unsigned)(a.B * a.H);
     const float c = a.scale * kLog2e;
     // dQ first: it also writes the row dots D that the dK/dV kernel reads.
     const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, CAUSAL>), gq, dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV, CAUSAL>), gq, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        static_cast<const T *>(a.o), b.Dsum, static_cast<T *>(b.dq), (int)a.N,
@@ -561,7 +651,7 @@ hipError_t launch3(const BwdArgs &b) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);
-    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, CAUSAL>), gk, dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, DV, CAUSAL>), gk, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        b.Dsum, static_cast<T *>(b.dk), static_cast<T *>(b.dv), (int)a.N,
@@ -569,20 +659,38 @@ hipError_t launch3(const BwdArgs &b) {
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 hipError_t launch2(const BwdArgs &b) {
-    return b.a.causal ? launch3<T, D, true>(b) : launch3<T, D, false>(b);
+    return b.a.causal ? launch3<T, D, DV, true>(b) : launch3<T, D, DV, false>(b);
+}
+
+template <typename T, int D>
+hipError_t launch_dv(const BwdArgs &b) {
+    switch (b.a.dv) {
+        case 32: return launch2<T, D, 32>(b);
+        case 64: return launch2<T, D, 64>(b);
+        case 128: return launch2<T, D, 128>(b);
+        case 256: return launch2<T, D, 256>(b);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename T>
 hipError_t launch1(const BwdArgs &b) {
-    return b.a.d == 64 ? launch2<T, 64>(b) : launch2<T, 128>(b);
+    switch (b.a.d) {
+        case 32: return launch_dv<T, 32>(b);
+        case 64: return launch_dv<T, 64>(b);
+        case 128: return launch_dv<T, 128>(b);
+        case 256: return launch_dv<T, 256>(b);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 bool bwd_mfma_supported(int dtype, int64_t d, int64_t dv) {
-    return (dtype == kBF16 || dtype == kF16) && d == dv && (d == 64 || d == 128);
+    auto ok = [](int64_t x) { return x == 32 || x == 64 || x == 128 || x == 256; };
+    return (dtype == kBF16 || dtype == kF16) && ok(d) && ok(dv);
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs &b) {

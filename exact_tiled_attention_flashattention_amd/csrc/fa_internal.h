@@ -67,7 +67,7 @@ int64_t decode_workgroups_per_split(int dtype, int64_t d, int64_t dv, int64_t B,
                                     int64_t rows);
 
 // Backward (fa_bwd.hip): row dots, then dQ and (dK, dV); the matrix-core
-// kernels (fa_bwd_mfma.hip) take bf16/fp16 with d == dv in {64, 128}.
+// kernels (fa_bwd_mfma.hip) take bf16/fp16 with d, dv in {32, 64, 128, 256}.
 hipError_t launch_bwd(const BwdArgs &b);
 bool bwd_mfma_supported(int dtype, int64_t d, int64_t dv);
 hipError_t launch_bwd_mfma(const BwdArgs &b);

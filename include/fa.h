@@ -216,10 +216,9 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
  *   workspace  device scratch of at least fa_bwd_workspace_size(B, H, N)
  *              bytes, 16-byte aligned, owned by the caller (the row dots D);
  *              contents on entry ignored, on exit undefined.
- * Arithmetic: products accumulated in float32; for bf16/fp16 with d = dv in
- * {64, 128} the probabilities and dS are rounded to `dtype` before the
- * products that use them (matrix cores), other shapes and fp32 stay in
- * float32 throughout.  Deterministic: every output element is written by
+ * Arithmetic: products accumulated in float32; for bf16/fp16 the
+ * probabilities and dS are rounded to `dtype` before the products that use
+ * them (matrix cores); fp32 stays in float32 throughout.  Deterministic: every output element is written by
  * one workgroup.  Returns FA_OK, FA_ERR_INVALID_ARG (as fa_fwd, plus null or
  * misaligned dout/dq/dk/dv), FA_ERR_UNSUPPORTED (as fa_fwd), FA_ERR_WORKSPACE
  * or FA_ERR_LAUNCH.
