@@ -112,8 +112,21 @@ def cpu_baseline(q, k, v, s, causal, heads: int):
     dt = time.perf_counter() - t0
     flops = credited_flops(s, causal) * heads / (s.B * s.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{heads} of {s.B * s.H} heads of {PREFILL} (FP64 standard attention, "
                       f"{flops / 1e9:.1f} GFLOP credited, {dt:.2f} s wall on {threads} threads)"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def summarize_pmc(directory: str) -> None:
@@ -614,6 +627,7 @@ def main() -> int:
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic["fwd"],
             "avg_launch_us": round(fwd_avg_s * 1e6, 2),
+            "median_launch_us": round(sorted(fwd_ms)[len(fwd_ms) // 2] * 1e3, 2),
             "min_launch_us": round(min(fwd_ms) * 1e3, 2),
             "credited_flop_per_launch": flops,
         },
@@ -630,6 +644,7 @@ def main() -> int:
                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                 "traffic": traffic["decode"],
                 "avg_launch_us": round(dec_avg_s * 1e6, 2),
+                "median_launch_us": round(sorted(dec_ms)[len(dec_ms) // 2] * 1e3, 2),
                 "min_launch_us": round(min(dec_ms) * 1e3, 2),
                 "algorithmic_bytes_per_launch": dbytes,
             },
