@@ -214,13 +214,18 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     const int nsteps = (N + QS - 1) / QS - s0;
 
     // Per-thread load slots: chunk t * kThreads + tid of [Q chunks | dO chunks].
+    // CHQ and CHQ + CHO are multiples of 64, so whether a slot is used and
+    // which tensor it reads is the same for a whole wave: derived from the
+    // wave index, the choice of buffer resource stays scalar.
+    static_assert(CHQ % 64 == 0 && (CHQ + CHO) % 64 == 0, "wave-uniform chunk roles");
     uint32_t gofs[NL], wA[NL], wT[NL];
     bool isdo[NL], used[NL];
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
         const int cidx = t * kThreads + tid;
-        used[t] = (CHQ + CHO) % kThreads == 0 || cidx < CHQ + CHO;
-        isdo[t] = cidx >= CHQ;
+        const int cwave = t * kThreads + wave * 64;
+        used[t] = cwave < CHQ + CHO;
+        isdo[t] = cwave >= CHQ;
         if constexpr (D == DV) {   // one layout for both tensors
             const int ch = cidx % CHQ;
             const int row = ch / CPRQ, cc = ch % CPRQ;
@@ -257,27 +262,29 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     for (int db = 0; db < DBV; ++db) rTo[db] = r0 * ROWO + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
 
     // Steps are fetched two ahead: step x's data waits in register set x % 2
-    // until it is stored to LDS stage x % 2 at the end of step x - 1.
+    // until it is stored to LDS stage x % 2 at the end of step x - 1.  The
+    // step's LSE and D are fetched the same way (bounds-checked: rows past N
+    // read 0; wave 0 stores them) and converted only when stored, so that
+    // nothing waits on the loads just issued.
+    const auto lrs = make_rsrc(Lh, (uint32_t)N * 4u);
+    const auto Drs = make_rsrc(Dh, (uint32_t)N * 4u);
     u32x4 regs0[NL], regs1[NL];
-    float val0 = 0.f, val1 = 0.f;
-    auto load_step = [&](u32x4 (&rg)[NL], float &val, int s) {   // global -> registers
+    float vl0 = 0.f, vd0 = 0.f, vl1 = 0.f, vd1 = 0.f;
+    auto load_step = [&](u32x4 (&rg)[NL], float &vl, float &vd, int s) {   // global -> registers
         const uint32_t baseq = (uint32_t)((s0 + s) * QS) * D * 2u;
         const uint32_t baseo = (uint32_t)((s0 + s) * QS) * DV * 2u;
+        // One load per slot with a (wave-uniform) choice of tensor; an unused
+        // slot fetches a harmless chunk that is never stored.
 #pragma unroll
         for (int t = 0; t < NL; ++t)
-            if (used[t])
-                rg[t] = isdo[t] ? buffer_load16(drs, baseo + gofs[t]) : buffer_load16(qrs, baseq + gofs[t]);
-        if (tid < 2 * QS) {
-            const int row = (s0 + s) * QS + (tid % QS);
-            if (tid < QS) {
-                const float L = row < N ? Lh[row] : -INFINITY;
-                val = L == -INFINITY ? INFINITY : L * kLog2e;   // +inf: no weight
-            } else {
-                val = row < N ? Dh[row] : 0.f;
-            }
-        }
+            rg[t] = buffer_load16(isdo[t] ? drs : qrs, (isdo[t] ? baseo : baseq) + gofs[t]);
+        // (every wave issues these two small loads, so that the count of
+        // loads per step, and with it every wait, is the same on all paths)
+        const uint32_t off = (uint32_t)((s0 + s) * QS + lane % QS) * 4u;
+        vl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (int)off, 0, 0));
+        vd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(Drs, (int)off, 0, 0));
     };
-    auto store_step = [&](const u32x4 (&rg)[NL], float val, int st) {   // registers -> LDS
+    auto store_step = [&](const u32x4 (&rg)[NL], float vl, float vd, int s, int st) {   // registers -> LDS
 #pragma unroll
         for (int t = 0; t < NL; ++t) {
             if (!used[t]) continue;
@@ -286,8 +293,12 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
             *reinterpret_cast<u32x4 *>(a + wA[t]) = rg[t];
             *reinterpret_cast<u32x4 *>(b + wT[t]) = rg[t];
         }
-        if (tid < QS) s_lse[st][tid] = val;
-        else if (tid < 2 * QS) s_D[st][tid - QS] = val;
+        if (tid < QS) {
+            const int row = (s0 + s) * QS + tid;
+            s_lse[st][tid] = (row >= N || vl == -INFINITY) ? INFINITY : vl * kLog2e;   // +inf: no weight
+        } else if (tid < 2 * QS) {
+            s_D[st][tid - QS] = vd;
+        }
     };
 
     f32x4 dka[DBK], dva[DBV];
@@ -368,21 +379,31 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         }
     };
 
+    // The prefetches are issued unconditionally (loads past the last step are
+    // bounds-checked and never stored), so that every path through the loop
+    // issues the same loads and each wait covers exactly what it needs.
     if (nsteps > 0) {
-        load_step(regs0, val0, 0);
-        store_step(regs0, val0, 0);
+        load_step(regs0, vl0, vd0, 0);
+        store_step(regs0, vl0, vd0, 0, 0);
     }
-    if (nsteps > 1) load_step(regs1, val1, 1);
+    load_step(regs1, vl1, vd1, 1);
+    // Re-define the K^T and V^T operands (landed by now) so that the step
+    // loop carries no dependence on their loads: it would otherwise wait on
+    // the vector-memory counter, and so on the steps' own prefetch loads.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kop[ks]));
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks) asm volatile("" : "+v"(vop[ks]));
     __syncthreads();
     for (int s = 0; s < nsteps; s += 2) {
-        if (s + 2 < nsteps) load_step(regs0, val0, s + 2);
+        load_step(regs0, vl0, vd0, s + 2);
         compute(s, 0);
-        if (s + 1 < nsteps) store_step(regs1, val1, 1);
+        if (s + 1 < nsteps) store_step(regs1, vl1, vd1, s + 1, 1);
         __syncthreads();
         if (s + 1 >= nsteps) break;
-        if (s + 3 < nsteps) load_step(regs1, val1, s + 3);
+        load_step(regs1, vl1, vd1, s + 3);
         compute(s + 1, 1);
-        if (s + 2 < nsteps) store_step(regs0, val0, 0);
+        if (s + 2 < nsteps) store_step(regs0, vl0, vd0, s + 2, 0);
         __syncthreads();
     }
 
@@ -481,13 +502,16 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     const int key_end = CAUSAL ? min(Nk, off_c + min(i0 + kWaves * 16, N)) : Nk;
     const int nsteps = key_end > 0 ? (key_end + BC - 1) / BC : 0;
 
+    // Chunk roles are uniform per wave (CHK and CHK + CHV are multiples of 64).
+    static_assert(CHK % 64 == 0 && (CHK + CHV) % 64 == 0, "wave-uniform chunk roles");
     uint32_t gofs[NL], wA[NL], wT[NL];
     bool isv[NL], used[NL];
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
         const int cidx = t * kThreads + tid;
-        used[t] = (CHK + CHV) % kThreads == 0 || cidx < CHK + CHV;
-        isv[t] = cidx >= CHK;
+        const int cwave = t * kThreads + wave * 64;
+        used[t] = cwave < CHK + CHV;
+        isv[t] = cwave >= CHK;
         if constexpr (D == DV) {   // one layout for both tensors
             const int ch = cidx % CHK;
             const int r = ch / CPRK, cc = ch % CPRK;
@@ -527,8 +551,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         const uint32_t basev = D == DV ? basek : (uint32_t)(s * BC) * DV * 2u;
 #pragma unroll
         for (int t = 0; t < NL; ++t)
-            if (used[t])
-                rg[t] = isv[t] ? buffer_load16(vrs, basev + gofs[t]) : buffer_load16(krs, basek + gofs[t]);
+            rg[t] = buffer_load16(isv[t] ? vrs : krs, (isv[t] ? basev : basek) + gofs[t]);
     };
     auto store_step = [&](const u32x4 (&rg)[NL], int st) {
 #pragma unroll
@@ -604,20 +627,26 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         }
     };
 
-    // Steps fetched two ahead, as in the dK/dV kernel.
+    // Steps fetched two ahead, unconditionally, as in the dK/dV kernel.
     if (nsteps > 0) {
         load_step(regs0, 0);
         store_step(regs0, 0);
     }
-    if (nsteps > 1) load_step(regs1, 1);
+    load_step(regs1, 1);
+    // As in the dK/dV kernel: the row's operands carry no load dependence
+    // into the step loop.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks) asm volatile("" : "+v"(dop[ks]));
     __syncthreads();
     for (int s = 0; s < nsteps; s += 2) {
-        if (s + 2 < nsteps) load_step(regs0, s + 2);
+        load_step(regs0, s + 2);
         compute(s, 0);
         if (s + 1 < nsteps) store_step(regs1, 1);
         __syncthreads();
         if (s + 1 >= nsteps) break;
-        if (s + 3 < nsteps) load_step(regs1, s + 3);
+        load_step(regs1, s + 3);
         compute(s + 1, 1);
         if (s + 2 < nsteps) store_step(regs0, 0);
         __syncthreads();
