@@ -447,10 +447,11 @@ def _time_call(torch, call, steps, warmup, stream):
 
 def bench_dims(args, torch, fa, si, dev) -> int:
     """Head dimensions outside d = dv in {64, 128}: causal bf16 prefill
-    (B16 x H16 x 2048) and decode (B8 x H32 x 32768, 64 splits) for several
-    (d, dv), next to d = dv = 128 on the matrix cores.  One JSON line with a
-    case list; TFLOP/s credited as 2 N Nk (d + dv) per head, halved for
-    causal; decode GB/s over K, V once plus q, o, lse."""
+    (B16 x H16 x 2048), decode (B8 x H32 x 32768, 64 splits) and backward
+    (B16 or B8 x H16 x 2048) for several (d, dv), next to d = dv = 128.  One
+    JSON line with a case list; TFLOP/s credited as 2 N Nk (d + dv) per head,
+    halved for causal (2.5 times that for the backward); decode GB/s over K,
+    V once plus q, o, lse."""
     stream = torch.cuda.current_stream(dev)
     cases = []
     for d, dv in [(128, 128), (64, 128), (128, 64), (256, 256)]:
@@ -477,6 +478,23 @@ def bench_dims(args, torch, fa, si, dev) -> int:
                       "splits": S, "us": round(t * 1e6, 1), "gbs": round(nbytes / t / 1e9, 1),
                       "frac_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)})
         del q, k, v
+    for (B, H, N, d, dv) in [(16, 16, 2048, 128, 128), (16, 16, 2048, 64, 128),
+                             (8, 16, 2048, 256, 256), (8, 16, 2048, 32, 32)]:
+        q, k, v = si.device_qkv(si.Shape(B, H, N, N, d, dv), 13, "bf16", dev, 0.5)
+        dout, _, _ = si.device_qkv(si.Shape(B, H, N, 1, dv, dv), 14, "bf16", dev, 1.0)
+        sc = 1.0 / math.sqrt(d)
+        o, lse = fa.fwd(q, k, v, causal=True, scale=sc)
+        ws = torch.empty(fa.bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
+        dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        t = _time_call(torch, lambda: fa.bwd(q, k, v, o, lse, dout, causal=True, scale=sc,
+                                             workspace=ws, dq=dq, dk=dk, dv=dvv),
+                       args.steps, args.warmup, stream)
+        flop = 2.5 * 2.0 * N * N * (d + dv) * B * H / 2
+        cases.append({"entry": "fa_bwd", "B": B, "H": H, "N": N, "d": d, "dv": dv,
+                      "causal": True, "us": round(t * 1e6, 1),
+                      "tflops": round(flop / t / 1e12, 1),
+                      "frac_bf16_peak": round(flop / t / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        del q, k, v, dout, o, lse, dq, dk, dvv
     print(json.dumps({"metric": "head-dimension coverage (median of HIP-event timings)",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
                       "data": "synthetic (seeded torch Philox draws on the GPU)",
