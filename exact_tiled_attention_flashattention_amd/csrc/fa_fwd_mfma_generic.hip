@@ -144,13 +144,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_generic_kernel(
     const int full = CAUSAL ? min(Nk, off_c + qw0 + 1) : Nk;
 
     // Per-thread load slots: chunk t * kThreads + tid of [K chunks | V chunks].
+    // CHK and CHK + CHV are multiples of 64, so a slot's use and tensor are
+    // the same for the whole wave: derived from the wave index, the choice of
+    // buffer resource stays scalar (a per-lane choice costs a loop per load).
+    static_assert(CHK % 64 == 0 && (CHK + CHV) % 64 == 0, "wave-uniform chunk roles");
     uint32_t gofs[NL], wofs[NL];
     bool isv[NL], used[NL];
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
         const int cidx = t * kThreads + tid;
-        used[t] = cidx < CHK + CHV;
-        isv[t] = cidx >= CHK;
+        const int cwave = t * kThreads + wave * 64;
+        used[t] = cwave < CHK + CHV;
+        isv[t] = cwave >= CHK;
         gofs[t] = 0;
         wofs[t] = 0;
         if (!used[t]) continue;
@@ -177,10 +182,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_generic_kernel(
     u32x4 regs0[NL], regs1[NL];
     auto load_step = [&](u32x4 (&rg)[NL], int s) {
         const uint32_t kb0 = (uint32_t)(s * kBC) * D * 2u, vb0 = (uint32_t)(s * kBC) * DV * 2u;
+        // One load per slot; an unused slot fetches a harmless chunk that is
+        // never stored.
 #pragma unroll
         for (int t = 0; t < NL; ++t)
-            if (used[t])
-                rg[t] = isv[t] ? buffer_load16(vrs, vb0 + gofs[t]) : buffer_load16(krs, kb0 + gofs[t]);
+            rg[t] = buffer_load16(isv[t] ? vrs : krs, (isv[t] ? vb0 : kb0) + gofs[t]);
     };
     auto store_step = [&](const u32x4 (&rg)[NL], int st) {
 #pragma unroll
@@ -257,19 +263,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_generic_kernel(
         }
     };
 
+    // Tiles are fetched two ahead, unconditionally: loads past the last tile
+    // are bounds-checked and never stored, so every path issues the same
+    // loads and each wait covers only what it needs.
     if (nsteps > 0) {
         load_step(regs0, 0);
         store_step(regs0, 0);
     }
-    if (nsteps > 1) load_step(regs1, 1);
+    load_step(regs1, 1);
+    // Re-define the Q operands (landed by now) so that the loop carries no
+    // dependence on their loads, which would make it wait on the vector-memory
+    // counter and so on its own prefetch.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qop[ks]));
     __syncthreads();
     for (int s = 0; s < nsteps; s += 2) {
-        if (s + 2 < nsteps) load_step(regs0, s + 2);
+        load_step(regs0, s + 2);
         compute(s, 0);
         if (s + 1 < nsteps) store_step(regs1, 1);
         __syncthreads();
         if (s + 1 >= nsteps) break;
-        if (s + 3 < nsteps) load_step(regs1, s + 3);
+        load_step(regs1, s + 3);
         compute(s + 1, 1);
         if (s + 2 < nsteps) store_step(regs0, 0);
         __syncthreads();
