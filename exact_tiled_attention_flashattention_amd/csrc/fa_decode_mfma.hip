@@ -162,11 +162,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
             qop[ks] = __builtin_bit_cast(vec8, raw);
         }
     };
+    // (The head index is uniform; readfirstlane says so to the compiler, which
+    // otherwise may hold the resource in vector registers and wrap every load
+    // in a loop over its distinct values.)
     auto k_rsrc = [&](int kvh) {
-        return make_rsrc(k + (int64_t)kvh * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+        const int h = __builtin_amdgcn_readfirstlane(kvh);
+        return make_rsrc(k + (int64_t)h * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
     };
     auto v_rsrc = [&](int kvh) {
-        return make_rsrc(v + (int64_t)kvh * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+        const int h = __builtin_amdgcn_readfirstlane(kvh);
+        return make_rsrc(v + (int64_t)h * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
     };
 
     // Per-lane byte offsets: global within a block (16-byte piece t * 64 +
