@@ -250,16 +250,27 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         }
     }
     // Per-lane read offsets.
-    uint32_t rAq[KS], rAo[KSV], rTq[DBK], rTo[DBV];
+    // The swizzles flip at most the low 4 bits of a 16-byte chunk index and
+    // the low 3 bits of a quad's 4-quad group, so past 16 chunks (4 read
+    // steps) or 8 column blocks the offsets repeat 256 bytes further on:
+    // only the first period is kept per lane (fewer registers at d = 256)
+    // and the rest is an immediate.
+    constexpr int NAQ = KS < 4 ? KS : 4, NAO = KSV < 4 ? KSV : 4;
+    constexpr int NTQ = DBK < 8 ? DBK : 8, NTO = DBV < 8 ? DBV : 8;
+    uint32_t rAq[NAQ], rAo[NAO], rTq[NTQ], rTo[NTO];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) rAq[ks] = li * ROWQ + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+    for (int ks = 0; ks < NAQ; ++ks) rAq[ks] = li * ROWQ + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
 #pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) rAo[ks] = li * ROWO + (((ks * 4 + g) ^ kswz<DV>(li)) * 16);
+    for (int ks = 0; ks < NAO; ++ks) rAo[ks] = li * ROWO + (((ks * 4 + g) ^ kswz<DV>(li)) * 16);
+    auto aq = [&](int ks) { return rAq[ks % NAQ] + (ks / NAQ) * 256; };
+    auto ao = [&](int ks) { return rAo[ks % NAO] + (ks / NAO) * 256; };
+    auto tq = [&](int db) { return rTq[db % NTQ] + (db / NTQ) * 256; };
+    auto to = [&](int db) { return rTo[db % NTO] + (db / NTO) * 256; };
     const int r0 = 4 * g + li / 4;
 #pragma unroll
-    for (int db = 0; db < DBK; ++db) rTq[db] = r0 * ROWQ + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+    for (int db = 0; db < NTQ; ++db) rTq[db] = r0 * ROWQ + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
 #pragma unroll
-    for (int db = 0; db < DBV; ++db) rTo[db] = r0 * ROWO + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
+    for (int db = 0; db < NTO; ++db) rTo[db] = r0 * ROWO + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
 
     // Steps are fetched two ahead: step x's data waits in register set x % 2
     // until it is stored to LDS stage x % 2 at the end of step x - 1.  The
@@ -322,16 +333,16 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
                 if constexpr (D == DV) {   // the two products interleaved step by step
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWQ + rAq[ks])), kop[ks], S[rb]);
-                        dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWO + rAq[ks])), vop[ks], dP[rb]);
+                        S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWQ + aq(ks))), kop[ks], S[rb]);
+                        dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWO + aq(ks))), vop[ks], dP[rb]);
                     }
                 } else {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWQ + rAq[ks])), kop[ks], S[rb]);
+                        S[rb] = Mma<T>::run(as_vec<T>(lds_row16(qa + rb * 16 * ROWQ + aq(ks))), kop[ks], S[rb]);
 #pragma unroll
                     for (int ks = 0; ks < KSV; ++ks)
-                        dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWO + rAo[ks])), vop[ks], dP[rb]);
+                        dP[rb] = Mma<T>::run(as_vec<T>(lds_row16(da + rb * 16 * ROWO + ao(ks))), vop[ks], dP[rb]);
                 }
             }
             // P and dS of rows rb*16 + 4g + r, key `key`.  Only steps where
@@ -365,16 +376,16 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
             if constexpr (D == DV) {
 #pragma unroll
                 for (int db = 0; db < DBK; ++db) {
-                    dva[db] = Mma<T>::run(lds_tr32<T, ROWO>(dt + rTq[db]), pb, dva[db]);
-                    dka[db] = Mma<T>::run(lds_tr32<T, ROWQ>(qt + rTq[db]), sb, dka[db]);
+                    dva[db] = Mma<T>::run(lds_tr32<T, ROWO>(dt + tq(db)), pb, dva[db]);
+                    dka[db] = Mma<T>::run(lds_tr32<T, ROWQ>(qt + tq(db)), sb, dka[db]);
                 }
             } else {
 #pragma unroll
                 for (int db = 0; db < DBV; ++db)
-                    dva[db] = Mma<T>::run(lds_tr32<T, ROWO>(dt + rTo[db]), pb, dva[db]);
+                    dva[db] = Mma<T>::run(lds_tr32<T, ROWO>(dt + to(db)), pb, dva[db]);
 #pragma unroll
                 for (int db = 0; db < DBK; ++db)
-                    dka[db] = Mma<T>::run(lds_tr32<T, ROWQ>(qt + rTq[db]), sb, dka[db]);
+                    dka[db] = Mma<T>::run(lds_tr32<T, ROWQ>(qt + tq(db)), sb, dka[db]);
             }
         }
     };
