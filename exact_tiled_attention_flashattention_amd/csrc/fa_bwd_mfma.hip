@@ -41,7 +41,9 @@
 // share the head's tensors through its L2.
 // Under the causal mask (query i at position Nk - N + i) each kernel walks
 // only the blocks some of its rows or keys can see, and a wave skips the
-// steps in which none of its own rows or keys is visible.
+// steps in which none of its own rows or keys is visible.  The kernels take
+// the offset of that diagonal (off_c = Nk - N); without the mask they run
+// with off_c = Nk, which makes every key visible to every row.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -154,11 +156,12 @@ template <int D, int DV> constexpr int bwd_waves_per_simd() { return D + DV <= 1
 // =============================================================================
 // dK, dV
 // =============================================================================
-template <typename T, int D, int DV, bool CAUSAL>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_dkdv_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dsum,
-    T *__restrict__ dk, T *__restrict__ dvo, int N, int Nk, float c, float scale, int heads) {
+    T *__restrict__ dk, T *__restrict__ dvo, int N, int Nk, int off_c, float c, float scale,
+    int heads) {
     typedef typename Mma<T>::vec vec8;
     constexpr int KS = D / 32;              // contraction steps of S = Q K^T (over d)
     constexpr int KSV = DV / 32;            // contraction steps of dP = dO V^T (over dv)
@@ -206,10 +209,8 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     for (int ks = 0; ks < KSV; ++ks)
         vop[ks] = as_vec<T>(buffer_load16(vrs, ((uint32_t)key * DV + ks * 32 + 8 * g) * 2u));
 
-    // Steps over query rows: all rows, or (causal) from the first row that
-    // sees key j0.
-    const int off_c = Nk - N;
-    const int first = CAUSAL ? max(0, j0 - off_c) : 0;
+    // Steps over query rows, from the first row that sees key j0.
+    const int first = max(0, j0 - off_c);
     const int s0 = first / QS;
     const int nsteps = (N + QS - 1) / QS - s0;
 
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     auto compute = [&](int s, int st) {
         const int i0 = (s0 + s) * QS;
         // Skip when no row of this step sees any of the wave's keys.
-        const bool active = !CAUSAL || kw0 <= off_c + i0 + QS - 1;
+        const bool active = kw0 <= off_c + i0 + QS - 1;
         if (active) {
             const unsigned char *qa = bq[st][0], *qt = bq[st][1];
             const unsigned char *da = bo[st][0], *dt = bo[st][1];
@@ -348,14 +349,14 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
             // P and dS of rows rb*16 + 4g + r, key `key`.  Only steps where
             // some of the wave's keys are hidden from some row (the diagonal,
             // or keys past Nk) pay for the mask.
-            const bool masked = kw0 + 15 >= Nk || (CAUSAL && kw0 + 15 > off_c + i0);
+            const bool masked = kw0 + 15 >= Nk || kw0 + 15 > off_c + i0;
             if (masked) {
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int rl = rb * 16 + 4 * g + r;
-                        const bool vis = key < Nk && (!CAUSAL || key <= off_c + i0 + rl);
+                        const bool vis = key < Nk && key <= off_c + i0 + rl;
                         const float p = vis ? fast_exp2(fmaf(S[rb][r], c, -s_lse[st][rl])) : 0.f;
                         S[rb][r] = p;
                         dP[rb][r] = p * (dP[rb][r] - s_D[st][rl]);
@@ -443,11 +444,12 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
 // =============================================================================
 // dQ
 // =============================================================================
-template <typename T, int D, int DV, bool CAUSAL>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_dq_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const T *__restrict__ o,
-    float *__restrict__ Dsum, T *__restrict__ dq, int N, int Nk, float c, float scale, int heads) {
+    float *__restrict__ Dsum, T *__restrict__ dq, int N, int Nk, int off_c, float c, float scale,
+    int heads) {
     typedef typename Mma<T>::vec vec8;
     constexpr int KS = D / 32;              // contraction steps of S^T = K Q^T (over d)
     constexpr int KSV = DV / 32;            // contraction steps of dP^T = V dO^T (over dv)
@@ -509,8 +511,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         if (g == 0) Dsum[(int64_t)head * N + row] = Drow;
     }
 
-    const int off_c = Nk - N;
-    const int key_end = CAUSAL ? min(Nk, off_c + min(i0 + kWaves * 16, N)) : Nk;
+    const int key_end = min(Nk, off_c + min(i0 + kWaves * 16, N));
     const int nsteps = key_end > 0 ? (key_end + BC - 1) / BC : 0;
 
     // Chunk roles are uniform per wave (CHK and CHK + CHV are multiples of 64).
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
 
     auto compute = [&](int s, int st) {
         const int j0 = s * BC;
-        const bool active = qw0 < N && (!CAUSAL || j0 <= off_c + qw0 + 15);
+        const bool active = qw0 < N && j0 <= off_c + qw0 + 15;
         if (active) {
             const unsigned char *ka = bk[st][0], *kt = bk[st][1], *va = bv[st];
             f32x4 S[KB], dP[KB];
@@ -608,14 +609,14 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
             }
             // As in the dK/dV kernel, only steps that reach past some row's
             // last visible key (or past Nk) apply the mask.
-            const bool masked = j0 + BC > Nk || (CAUSAL && j0 + BC - 1 > off_c + qw0);
+            const bool masked = j0 + BC > Nk || j0 + BC - 1 > off_c + qw0;
             if (masked) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int kk = j0 + kb * 16 + 4 * g + r;
-                        const bool vis = kk < Nk && (!CAUSAL || kk <= off_c + row);
+                        const bool vis = kk < Nk && kk <= off_c + row;
                         const float p = vis ? fast_exp2(fmaf(S[kb][r], c, -lse2)) : 0.f;
                         dP[kb][r] = p * (dP[kb][r] - Drow);
                     }
@@ -676,32 +677,31 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     }
 }
 
-template <typename T, int D, int DV, bool CAUSAL>
-hipError_t launch3(const BwdArgs &b) {
+// Query i sees keys up to off_c + i: off_c = Nk - N under the causal mask
+// (bottom-right), and off_c = Nk (every key) without it, so one kernel per
+// shape serves both.
+template <typename T, int D, int DV>
+hipError_t launch2(const BwdArgs &b) {
     const FwdArgs &a = b.a;
     const unsigned heads = (unsigned)(a.B * a.H);
     const float c = a.scale * kLog2e;
+    const int off_c = a.causal ? (int)(a.Nk - a.N) : (int)a.Nk;
     // dQ first: it also writes the row dots D that the dK/dV kernel reads.
     const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV, CAUSAL>), gq, dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV>), gq, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        static_cast<const T *>(a.o), b.Dsum, static_cast<T *>(b.dq), (int)a.N,
-                       (int)a.Nk, c, a.scale, (int)heads);
+                       (int)a.Nk, off_c, c, a.scale, (int)heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);
-    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, DV, CAUSAL>), gk, dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, DV>), gk, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
                        b.Dsum, static_cast<T *>(b.dk), static_cast<T *>(b.dv), (int)a.N,
-                       (int)a.Nk, c, a.scale, (int)heads);
+                       (int)a.Nk, off_c, c, a.scale, (int)heads);
     return hipGetLastError();
-}
-
-template <typename T, int D, int DV>
-hipError_t launch2(const BwdArgs &b) {
-    return b.a.causal ? launch3<T, D, DV, true>(b) : launch3<T, D, DV, false>(b);
 }
 
 template <typename T, int D>
