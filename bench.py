@@ -248,21 +248,24 @@ def summarize_trace(directory: str) -> None:
         print("\n".join(lines))
 
 
-GQA = dict(B=8, Hq=32, Hkv=8, Nk=32768, d=128, num_splits=64, seed_q=41, seed_kv=42)
+GQA = dict(B=8, Hq=32, Hkv=8, Nk=32768, d=128, num_splits=0, seed_q=41, seed_kv=42)   # 0: automatic
 GQA_WORKLOAD = "decode_gqa_b8_hq32_hkv8_nk32768_d128"
 
 
 def bench_gqa(args, torch, fa, si, dev) -> int:
     """Grouped-query split-KV decode: 4 query heads per key/value head, the
-    long-context decode size with 8 key/value heads.  Algorithmic bytes are K
-    and V once per key/value head plus Q, O (bf16) and LSE (fp32)."""
+    long-context decode size with 8 key/value heads, with the automatic split
+    count (num_splits = 0).  Algorithmic bytes are K and V once per key/value
+    head plus Q, O (bf16) and LSE (fp32)."""
     g = GQA
     q, _, _ = si.device_qkv(si.Shape(g["B"], g["Hq"], 1, 1, g["d"], g["d"]), g["seed_q"], "bf16", dev)
     _, k, v = si.device_qkv(si.Shape(g["B"], g["Hkv"], 1, g["Nk"], g["d"], g["d"]), g["seed_kv"],
                             "bf16", dev)
     o = torch.empty((g["B"], g["Hq"], 1, g["d"]), dtype=q.dtype, device=dev)
     lse = torch.empty((g["B"], g["Hq"], 1), dtype=torch.float32, device=dev)
-    ws = torch.empty(fa.decode_splitkv_workspace_size(g["B"], g["Hq"], 1, g["d"], g["num_splits"]),
+    splits = g["num_splits"] or fa.decode_splitkv_auto_splits(g["B"], g["Hq"], g["Hkv"], 1, g["Nk"],
+                                                               g["d"], g["d"], torch.bfloat16)
+    ws = torch.empty(fa.decode_splitkv_workspace_size(g["B"], g["Hq"], 1, g["d"], splits),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -293,7 +296,8 @@ def bench_gqa(args, torch, fa, si, dev) -> int:
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded torch Philox draws on the GPU)",
         "config": {"workload": GQA_WORKLOAD, **{k2: v2 for k2, v2 in g.items()
-                                                                        if not k2.startswith("seed")}},
+                                                if not k2.startswith("seed")},
+                   "splits_used": splits},
         "roofline": {"kernel": "decode_segment_mfma_kernel<bf16,128> + decode_merge_kernel",
                      "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
