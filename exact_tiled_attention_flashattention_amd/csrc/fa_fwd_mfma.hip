@@ -125,8 +125,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     constexpr int LPT = TILE / 1024 / kWaves;   // 1 KiB wave loads per wave per K tile
     constexpr int LPTV = TILEV / 1024 / kWaves; // ... per V tile
     static_assert(LPT * 1024 * kWaves == TILE && LPTV * 1024 * kWaves == TILEV, "tile split");
-    __shared__ __attribute__((aligned(16))) unsigned char kbuf[NK][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char vbuf[NV][TILEV];
+    // K stages, then V stages, in one array.  After an item's tile loop
+    // (whose last barrier every wave has passed, with no copy in flight) the
+    // same memory holds each wave's normalised output rows on the way out,
+    // so that every store instruction writes whole rows (1 KiB contiguous at
+    // dv = 64) instead of 8-byte pieces of 16 rows.  Those rows are padded by
+    // 16 bytes, which spreads the 8-byte writes of one column over the banks.
+    constexpr int OPITCH = DV * 2 + 16;
+    static_assert(kWaves * kQW * OPITCH <= NK * TILE + NV * TILEV, "output staging fits");
+    __shared__ __attribute__((aligned(16))) unsigned char kvbuf[NK * TILE + NV * TILEV];
+    unsigned char(*kbuf)[TILE] = reinterpret_cast<unsigned char(*)[TILE]>(kvbuf);
+    unsigned char(*vbuf)[TILEV] = reinterpret_cast<unsigned char(*)[TILEV]>(kvbuf + NK * TILE);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform per wave
@@ -499,22 +508,44 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
+    // The wave's 32 x dv tile is written to its LDS slice (lane: row
+    // qb*16 + li, columns 16 db + 4g .. +3), read back row-major 16 bytes per
+    // lane, and stored as whole rows.
+    // (The lane index is re-defined through an empty asm so that none of the
+    // epilogue's address arithmetic is hoisted into the tile loops, where it
+    // would hold registers.)
+    unsigned char *ow = kvbuf + wave * (kQW * OPITCH);
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int eli = elane % 16, eg = elane / 16;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float lt = lacc[qb][0];
-        const int qi = qw0 + qb * 16 + li;
-        if (qi >= N) continue;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        T *orow = o + ((int64_t)head * N + qi) * DV;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             typedef T t4 __attribute__((ext_vector_type(4)));
             t4 out;
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[r] = static_cast<T>(oacc[db][qb][r] * inv);
-            *reinterpret_cast<t4 *>(orow + db * 16 + 4 * g) = out;
+            *reinterpret_cast<t4 *>(ow + (qb * 16 + eli) * OPITCH + (db * 16 + 4 * eg) * 2) = out;
         }
-        if (g == 0) lse[(int64_t)head * N + qi] = lt > 0.f ? (m[qb] + fast_log2(lt)) * kLn2 : -INFINITY;
+        const int qi = qw0 + qb * 16 + eli;
+        if (eg == 0 && qi < N)
+            lse[(int64_t)head * N + qi] = lt > 0.f ? (m[qb] + fast_log2(lt)) * kLn2 : -INFINITY;
+    }
+    {
+        constexpr int CPRO = DV * 2 / 16;            // 16-byte chunks per output row
+        constexpr int RPI = 64 / CPRO;               // rows per store instruction
+        const int rr = elane / CPRO, cc = elane % CPRO;
+#pragma unroll
+        for (int t = 0; t < kQW / RPI; ++t) {
+            const int row = t * RPI + rr;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(ow + row * OPITCH + cc * 16);
+            const int qi = qw0 + row;
+            if (qi < N)
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(o + ((int64_t)head * N + qi) * DV) + cc * 16) = val;
+        }
     }
     }   // item loop
 }
