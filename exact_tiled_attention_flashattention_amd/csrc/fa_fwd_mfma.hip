@@ -507,6 +507,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
         }
     }
 
+    const auto ors = make_rsrc(o + (int64_t)head * N * DV, (uint32_t)N * DV * 2u);
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
     // The wave's 32 x dv tile is written to its LDS slice (lane: row
     // qb*16 + li, columns 16 db + 4g .. +3), read back row-major 16 bytes per
@@ -543,8 +544,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
             const int row = t * RPI + rr;
             const u32x4 val = *reinterpret_cast<const u32x4 *>(ow + row * OPITCH + cc * 16);
             const int qi = qw0 + row;
-            if (qi < N)
-                *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(o + ((int64_t)head * N + qi) * DV) + cc * 16) = val;
+            // Bounds-checked store (rows past N fall outside the buffer and
+            // are dropped) with the non-temporal hint: O is not read again.
+            __builtin_amdgcn_raw_buffer_store_b128(val, ors, (int)(((uint32_t)qi * DV) * 2u + cc * 16), 0, 2);
         }
     }
     }   // item loop
