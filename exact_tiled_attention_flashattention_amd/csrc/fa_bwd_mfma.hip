@@ -149,48 +149,6 @@ __device__ __forceinline__ typename Mma<T>::vec pack_b(f32x4 a, f32x4 b) {
     return r;
 }
 
-// Stores a wave's 16 x W result tile (W = D or DV columns) as whole rows.
-// acc[db] holds the transposed 16x16 block db: lane (li, g) has columns
-// 16 db + 4g .. +3 of row li.  The lane's 8 bytes go to the wave's LDS slice
-// `buf` (16 rows of ROWB = 2 W bytes, 16-byte chunks XOR-swizzled by the row
-// so that the writes of one column spread over the banks); the wave then
-// reads the tile back 16 bytes per lane in row order and stores each row
-// chunk with a bounds-checked, non-temporal buffer store (rows at or past
-// the buffer's end are dropped).  row0 is the tile's first row in `rs`.
-// Every lane of the wave must call it; the caller makes sure that no other
-// wave still reads `buf`.
-template <typename T, int W, int ROWB, int NB>
-__device__ __forceinline__ void store_rows(unsigned char *buf, int lane, int rows,
-                                           const f32x4 (&acc)[NB], float mul,
-                                           __amdgpu_buffer_rsrc_t rs, int row0) {
-    typedef T t4 __attribute__((ext_vector_type(4)));
-    constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
-    constexpr int SW = CPR < 8 ? CPR : 8;        // swizzle period
-    static_assert(NB == W / 16 && ROWB == 2 * W, "tile shape");
-    // (the lane index is re-defined so that none of this address arithmetic
-    // is hoisted into the caller's loops)
-    int el = lane;
-    asm volatile("" : "+v"(el));
-    const int li = el % 16, g = el / 16;
-#pragma unroll
-    for (int db = 0; db < NB; ++db) {
-        t4 a;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = static_cast<T>(acc[db][r] * mul);
-        const int chunk = (2 * db + g / 2) ^ (li % SW);
-        *reinterpret_cast<t4 *>(buf + li * ROWB + chunk * 16 + (g % 2) * 8) = a;
-    }
-    constexpr int RPI = 64 / CPR;                // rows per store instruction
-    const int rr = el / CPR, cc = el % CPR;
-#pragma unroll
-    for (int t = 0; t < 16 / RPI; ++t) {
-        const int r = t * RPI + rr;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + r * ROWB + ((cc ^ (r % SW)) * 16));
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)((uint32_t)(row0 + r) * ROWB + cc * 16), 0, 2);
-    }
-    (void)rows;
-}
-
 // Waves per SIMD the launch bounds ask for: 4 (two resident workgroups per
 // CU, at most 128 registers) for the small head dimensions, 2 otherwise.
 template <int D, int DV> constexpr int bwd_waves_per_simd() { return D + DV <= 128 ? 4 : 2; }
@@ -465,9 +423,9 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     // They leave through LDS (the step buffers are idle after the loop's last
     // barrier: the Q buffer holds the workgroup's 128 dK rows exactly, the dO
     // buffer its dV rows), read back row-major and stored as whole rows.
-    store_rows<T, D, ROWQ>(&bq[0][0][0] + wave * 16 * ROWQ, lane, 16, dka, scale,
+    store_rows<T, D, ROWQ>(&bq[0][0][0] + wave * 16 * ROWQ, lane, dka, scale,
                            make_rsrc(dk + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u), kw0);
-    store_rows<T, DV, ROWO>(&bo[0][0][0] + wave * 16 * ROWO, lane, 16, dva, 1.f,
+    store_rows<T, DV, ROWO>(&bo[0][0][0] + wave * 16 * ROWO, lane, dva, 1.f,
                             make_rsrc(dvo + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u), kw0);
 }
 
@@ -697,7 +655,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     // dQ^T leaves through LDS like dK and dV (the K buffer is idle after the
     // loop's last barrier and holds the workgroup's 128 rows).
     static_assert(sizeof(bk) >= kWaves * 16 * ROWK, "dQ staging fits");
-    store_rows<T, D, ROWK>(&bk[0][0][0] + wave * 16 * ROWK, lane, 16, dqa, scale,
+    store_rows<T, D, ROWK>(&bk[0][0][0] + wave * 16 * ROWK, lane, dqa, scale,
                            make_rsrc(dq + (int64_t)head * N * D, (uint32_t)N * D * 2u), qw0);
 }
 

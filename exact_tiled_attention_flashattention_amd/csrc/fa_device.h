@@ -116,4 +116,45 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_
                  : "memory", "m0");
 }
 
+// Stores a wave's 16 x W result tile (W = D or DV columns) as whole rows.
+// acc[db] holds the transposed 16x16 block db: lane (li, g) has columns
+// 16 db + 4g .. +3 of row li, which are multiplied by `mul` (per lane).  The lane's 8 bytes go to the wave's LDS slice
+// `buf` (16 rows of ROWB = 2 W bytes, 16-byte chunks XOR-swizzled by the row
+// so that the writes of one column spread over the banks); the wave then
+// reads the tile back 16 bytes per lane in row order and stores each row
+// chunk with a bounds-checked, non-temporal buffer store (rows at or past
+// the buffer's end are dropped).  row0 is the tile's first row in `rs`.
+// Every lane of the wave must call it; the caller makes sure that no other
+// wave still reads `buf`.
+template <typename T, int W, int ROWB, int NB, typename AccV>
+__device__ __forceinline__ void store_rows(unsigned char *buf, int lane, const AccV (&acc)[NB],
+                                           float mul,
+                                           __amdgpu_buffer_rsrc_t rs, int row0) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+    constexpr int SW = CPR < 8 ? CPR : 8;        // swizzle period
+    static_assert(NB == W / 16 && ROWB == 2 * W, "tile shape");
+    // (the lane index is re-defined so that none of this address arithmetic
+    // is hoisted into the caller's loops)
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int li = el % 16, g = el / 16;
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+        t4 a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = static_cast<T>(acc[db][r] * mul);
+        const int chunk = (2 * db + g / 2) ^ (li % SW);
+        *reinterpret_cast<t4 *>(buf + li * ROWB + chunk * 16 + (g % 2) * 8) = a;
+    }
+    constexpr int RPI = 64 / CPR;                // rows per store instruction
+    const int rr = el / CPR, cc = el % CPR;
+#pragma unroll
+    for (int t = 0; t < 16 / RPI; ++t) {
+        const int r = t * RPI + rr;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + r * ROWB + ((cc ^ (r % SW)) * 16));
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)((uint32_t)(row0 + r) * ROWB + cc * 16), 0, 2);
+    }
+}
+
 }  // namespace fa

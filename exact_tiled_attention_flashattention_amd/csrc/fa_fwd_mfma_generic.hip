@@ -291,20 +291,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_generic_kernel(
 
     // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2; a row with no visible
     // key gets O = 0 and LSE = -inf.
+    // O leaves through LDS (the V stage buffers are idle after the loop's last
+    // barrier and hold the workgroup's 64 rows) and is stored as whole rows.
     const float lt = rows4_sum(l);
-    if (row < N) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        T *orow = o + ((int64_t)head * N + row) * DV;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            typedef T t4 __attribute__((ext_vector_type(4)));
-            t4 out;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) out[r] = static_cast<T>(oacc[db][r] * inv);
-            *reinterpret_cast<t4 *>(orow + 16 * db + 4 * g) = out;
-        }
-        if (g == 0) lse[(int64_t)head * N + row] = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
-    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row < N && g == 0) lse[(int64_t)head * N + row] = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+    static_assert(sizeof(vbuf) >= kWaves * 16 * ROWV, "output staging fits");
+    store_rows<T, DV, ROWV>(&vbuf[0][0] + wave * 16 * ROWV, lane, oacc, inv,
+                            make_rsrc(o + (int64_t)head * N * DV, (uint32_t)N * DV * 2u), qw0);
 }
 
 template <typename T, int D, int DV>
