@@ -358,8 +358,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
                         if (kb * 16 + r > t) s[kb][qb][r] = -INFINITY;
             }
         }
-        float mt[2];
-        bool need[2];
+        // A row's tile maximum exceeds m + 8 exactly when the maximum over one
+        // of its four lanes' scores does, so the wave tests its lanes' own
+        // maxima and forms the row maxima (a cross-lane reduction) only in
+        // the rare case that some row moves.
+        float xl[2];
+        bool any[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             float x = s[0][qb][0];
@@ -367,15 +371,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x = __builtin_elementwise_maximum(x, s[kb][qb][r]);
-            mt[qb] = rows_max(x) * c;
-            need[qb] = mt[qb] > m[qb] + 8.f;
+            xl[qb] = x;
+            any[qb] = x * c > m[qb] + 8.f;
         }
-        if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
+        if (__builtin_amdgcn_ballot_w64(any[0] || any[1])) {
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const float m_new = need[qb] ? mt[qb] : m[qb];
+                const float mt = rows_max(xl[qb]) * c;
+                const bool need = mt > m[qb] + 8.f;
+                const float m_new = need ? mt : m[qb];
                 const float alpha = fast_exp2(m[qb] - m_new);   // 0 when m = -inf < m_new
-                const float a = need[qb] ? alpha : 1.f;
+                const float a = need ? alpha : 1.f;
                 lacc[qb] *= a;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[db][qb] *= a;
