@@ -390,12 +390,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma32_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) x = __builtin_elementwise_maximum(x, sb[P][kb][r]);
-        const float mt = halves_max(x) * c;
-        const bool need = mt > m + 8.f;
-        const float m_new = need ? mt : m;
-        const float a = need ? fast_exp2(m - m_new) : 1.f;   // 0 when m = -inf < m_new
-        l *= a;
-        m = m_new;
+        // The row's tile maximum exceeds m + 8 exactly when one of its two
+        // lanes' maxima does: the row maximum (a lane exchange) is formed
+        // only in the rare case that some row of the wave moves.
+        float a = 1.f;
+        if (__builtin_amdgcn_ballot_w64(x * c > m + 8.f)) {
+            const float mt = halves_max(x) * c;
+            const bool need = mt > m + 8.f;
+            const float m_new = need ? mt : m;
+            a = need ? fast_exp2(m - m_new) : 1.f;   // 0 when m = -inf < m_new
+            l *= a;
+            m = m_new;
+        }
         const float m_use = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
