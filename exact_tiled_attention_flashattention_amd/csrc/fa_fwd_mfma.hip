@@ -273,6 +273,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     }
 
     float m[2] = {-INFINITY, -INFINITY};   // running max of scaled scores (base 2)
+    // Kept with m, changed only when m moves: the exponent offset (0 while
+    // m = -inf) and the rescale threshold m + 8.
+    float mu[2] = {0.f, 0.f}, m8[2] = {-INFINITY, -INFINITY};
     f32x4 lacc[2];                         // row sums (every register holds the sum)
     f32x4 oacc[DB][2];
 #pragma unroll
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) x = __builtin_elementwise_maximum(x, s[kb][qb][r]);
             xl[qb] = x;
-            any[qb] = x * c > m[qb] + 8.f;
+            any[qb] = x * c > m8[qb];
         }
         if (__builtin_amdgcn_ballot_w64(any[0] || any[1])) {
 #pragma unroll
@@ -386,11 +389,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[db][qb] *= a;
                 m[qb] = m_new;
+                mu[qb] = m_new == -INFINITY ? 0.f : m_new;
+                m8[qb] = m_new + 8.f;
             }
         }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const float m_use = (m[qb] == -INFINITY) ? 0.f : m[qb];
+            const float m_use = mu[qb];
 #pragma unroll
             for (int pc = 0; pc < PC; ++pc) {
                 f32x8 pf;
