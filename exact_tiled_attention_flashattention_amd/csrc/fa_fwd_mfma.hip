@@ -92,6 +92,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// 16-byte buffer load into registers, issued as inline assembly so that the
+// compiler does not track it: the caller waits for it with an explicit
+// s_waitcnt vmcnt before the first use of the result.  Out-of-range offsets
+// read zeros.
+__device__ __forceinline__ u32x4 load16_untracked(u32x4 rsrc, uint32_t voff) {
+    u32x4 r;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rsrc) : "memory");
+    return r;
+}
+
 // LDS swizzles.  K: 16-byte chunk c of key row r is stored at chunk
 // c ^ kswz(r).  V: 8-byte quad u of row r is stored at quad u ^ vswz(r)
 // (a multiple of 4, so 16-byte chunks stay whole).
@@ -193,9 +203,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     const int qw0 = q0 + grp * (kBR / 2) + (wave % 4) * kQW;
 
     // Bounds-checked views of this head's Q, K, V (reads past the end give 0).
-    const auto qrs = make_rsrc(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
+    const u32x4 qw = rsrc_words(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
 
     // ---- Q^T operands: lane holds Q[qw0 + qb*16 + li][ks*32 + 8g .. +7] ---
+    // (untracked loads: the first wait below covers them, so that the tile
+    // loop does not start with a wait for every load in flight)
     vec8 qop[2][KS];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -203,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const uint32_t off = ((uint32_t)row * D + ks * 32 + 8 * g) * 2u;
-            qop[qb][ks] = __builtin_bit_cast(vec8, buffer_load16(qrs, off));
+            qop[qb][ks] = __builtin_bit_cast(vec8, load16_untracked(qw, off));
         }
     }
 
@@ -456,9 +468,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(
     issue_v(0);
     issue_k(2);
     issue_v(1);
-    wait_vmcnt<0>();
-    // Re-define the Q operands here so that the loops carry no dependence on
-    // their loads (they would otherwise wait for every outstanding load).
+    // Wait for Q and K tile 0 only: the copies issued after K tile 0 may
+    // still be in flight (loads complete in order, so at most that many
+    // outstanding means everything before them has landed).  The first
+    // load step waits for K tile 1 and V tile 0.
+    if (ntiles >= 3) wait_vmcnt<2 * LPT + 2 * LPTV>();
+    else if (ntiles == 2) wait_vmcnt<LPT + 2 * LPTV>();
+    else if (ntiles == 1) wait_vmcnt<LPTV>();
+    else wait_vmcnt<0>();
+    // Re-define the Q operands here so that they are read only after that
+    // wait and the loops carry no dependence on their loads.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
