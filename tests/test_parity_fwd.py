@@ -39,7 +39,7 @@ def test_ragged_f32(shape, causal):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("N,Nk", [(300, 300), (77, 513), (513, 77), (1, 1000), (256, 256),
-                                  (129, 1), (1, 1)])
+                                  (129, 1), (1, 1), (64, 64), (100, 150)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_small_multi_tile(dtype, d, N, Nk, causal):
     _run(2, 3, N, Nk, d, dtype, causal, seed=N * 7 + Nk + d)
