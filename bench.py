@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0          # HBM3E
 PREFILL = "prefill_b64_h16_n1024_d64"
 DECODE = "decode_b8_h32_nk32768_d128"
 FWD_KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc",
-                              "fa_fwd_mfma.hip")
+                              "fa_fwd_mfma_wide.hip")
 DEC_KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc",
                               "fa_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
@@ -149,7 +149,7 @@ def summarize_pmc(directory: str) -> None:
         vals = values(counter, pred)
         return sum(vals) / len(vals) if vals else None
 
-    is_fwd = lambda n: "fwd_mfma_kernel" in n
+    is_fwd = lambda n: "fwd_mfma32_kernel" in n
     is_seg = lambda n: "decode_segment_kernel" in n
     is_merge = lambda n: "decode_merge_kernel" in n
     # The 1 GiB calibration copy is a device-to-device memcpy; it is by far the
@@ -219,7 +219,7 @@ def summarize_trace(directory: str) -> None:
                "fa_bwd calls)")
     # file -> (kernel that must be in the trace, kernels listed, command)
     groups = {
-        f"fwd_mfma_kernel_{PREFILL}.txt": ("fwd_mfma_kernel", ("fwd_mfma_kernel",), default_cmd),
+        f"fwd_mfma32_kernel_{PREFILL}.txt": ("fwd_mfma32_kernel", ("fwd_mfma32_kernel",), default_cmd),
         f"decode_splitkv_{DECODE}.txt": ("decode_segment_kernel",
                                          ("decode_segment_kernel", "decode_merge_kernel"),
                                          default_cmd),
@@ -655,7 +655,7 @@ def main() -> int:
                        "num_splits": wd.num_splits},
         },
         "roofline": {
-            "kernel": "fwd_mfma_kernel<bf16,64,causal>",
+            "kernel": "fwd_mfma32_kernel<bf16,64,causal>",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

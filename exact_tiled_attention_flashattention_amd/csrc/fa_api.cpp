@@ -133,7 +133,7 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, void *o, float *
     // the tuned matrix-core kernels where they apply, else the generic one.
     hipError_t e = dtype == FA_DTYPE_F32                         ? fa::launch_fwd_rowwise(a)
                    : !fa::fwd_mfma_supported(a.dtype, d, dv, scale) ? fa::launch_fwd_mfma_generic(a)
-                   : (d == 128 && dv == 128)                       ? fa::launch_fwd_mfma_d128(a)
+                   : fa::fwd_wide_preferred(d, dv, Nk)              ? fa::launch_fwd_mfma_wide(a)
                                                                    : fa::launch_fwd_mfma16(a);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -1,7 +1,7 @@
 // fa_fwd_mfma_wide.hip -- exact attention forward on the CDNA4 matrix cores,
-// head dimension 128.
+// head dimension 128, and head dimension 64 over short key ranges.
 //
-// bf16/fp16 inputs, d == dv == 128, scale > 0; fp32 accumulation.
+// bf16/fp16 inputs, d == dv in {64, 128}, scale > 0; fp32 accumulation.
 //
 // Method: the FlashAttention-2 loop order of CS349E Lecture 11
 // "flash_lab.py", section 3 (flash_fwd, order "fa2"): one block of 256
@@ -39,6 +39,13 @@
 //  * The kernel is persistent: each workgroup walks units of two query
 //    blocks of one head whose causal costs add up to a constant, numbered
 //    so that workgroups of one XCD share heads (K/V reuse in that L2).
+//  * At d = 64 the kernel needs 80 KiB of LDS and about 125 registers, so
+//    two workgroups share a CU.  Their items start and end at different
+//    times, and one workgroup's item boundary (Q and first tiles in
+//    flight, output stores) overlaps the other's tile loop.  That wins
+//    over the one-workgroup ping-pong kernel of fa_fwd_mfma.hip while items
+//    are short (up to about 48 key tiles); the ping-pong's vector/matrix
+//    alternation wins on longer key ranges.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma32_kernel(
     T *__restrict__ o, float *__restrict__ lse, int N, int Nk, float c,
     int q_blocks, int n_items) {
     typedef typename Mfma<T>::vec vec8;
-    static_assert(D == 128, "this kernel is the d = 128 variant");
+    static_assert(D == 128 || D == 64, "d = dv = 64 or 128");
     constexpr int KLEAD = 2;                    // K tiles fetched ahead of the tile being consumed
     constexpr int KS = D / 16;                  // 16-wide contraction steps of S (d)
     constexpr int DB = D / 32;                  // 32-wide value blocks of O
@@ -585,12 +592,20 @@ hipError_t launch2(const FwdArgs &a) {
 
 template <typename T>
 hipError_t launch1(const FwdArgs &a) {
-    return launch2<T, 128>(a);
+    if (a.d == 128 && a.dv == 128) return launch2<T, 128>(a);
+    if (a.d == 64 && a.dv == 64) return launch2<T, 64>(a);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma_d128(const FwdArgs &a) {
+bool fwd_wide_preferred(int64_t d, int64_t dv, int64_t Nk) {
+    // d = 64: crossover measured at Nk = 3072 (B16 x H16, causal, equal times);
+    // below it the two-workgroup kernel is 5-20% faster, above it 2-7% slower.
+    return (d == 128 && dv == 128) || (d == 64 && dv == 64 && Nk <= 3072);
+}
+
+hipError_t launch_fwd_mfma_wide(const FwdArgs &a) {
     return a.dtype == kBF16 ? launch1<bf16_t>(a) : launch1<f16_t>(a);
 }
 

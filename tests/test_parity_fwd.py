@@ -45,6 +45,15 @@ def test_small_multi_tile(dtype, d, N, Nk, causal):
     _run(2, 3, N, Nk, d, dtype, causal, seed=N * 7 + Nk + d)
 
 
+# d = dv = 64 runs on the two-workgroup 32x32 kernel up to 3072 keys and on
+# the ping-pong 16x16 kernel beyond; these shapes sit on both sides.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N,Nk", [(300, 3072), (300, 3073), (3200, 3200), (1, 4100)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d64_key_range_dispatch(dtype, N, Nk, causal):
+    _run(1, 2, N, Nk, 64, dtype, causal, seed=N + Nk)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_scale_zero_is_mean_of_visible_values(dtype):
     _run(1, 2, 200, 333, 64, dtype, True, seed=9, scale=0.0)
