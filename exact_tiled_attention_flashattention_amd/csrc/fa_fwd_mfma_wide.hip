@@ -40,7 +40,7 @@
 //    blocks of one head whose causal costs add up to a constant, numbered
 //    so that workgroups of one XCD share heads (K/V reuse in that L2).
 //  * At d = 64 the kernel needs 80 KiB of LDS and about 125 registers, so
-//    two workgroups share a CU.  Their items start and end at different
+//    two workgroups share a CU (the launch bounds ask for two there).  Their items start and end at different
 //    times, and one workgroup's item boundary (Q and first tiles in
 //    flight, output stores) overlaps the other's tile loop.  That wins
 //    over the one-workgroup ping-pong kernel of fa_fwd_mfma.hip while items
@@ -203,7 +203,7 @@ __device__ __forceinline__ void wait_pending(int n) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_mfma32_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void fwd_mfma32_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     T *__restrict__ o, float *__restrict__ lse, int N, int Nk, float c,
     int q_blocks, int n_items) {
