@@ -71,3 +71,22 @@ def test_gqa_largest_head_slice():
         ls_.append(r[1])
     import numpy as np
     _check(o, lse, np.stack(os_), np.stack(ls_), heads, f"gqa Nk={nk}")
+
+
+def test_bwd_largest_head_slice():
+    # One head is checked (the second, past 2 GiB): the oracle's gradients of
+    # a slice this long take tens of GB of host memory in fp64.
+    from tests.parity import compare_grads, oracle_bwd_on
+    d = 128
+    s = si.Shape(1, 2, 8, _largest_nk(d), d, d)
+    log(f"fa_bwd largest head slice B=1 H=2 N=8 Nk={s.Nk} d={d} causal")
+    q, k, v = si.device_qkv(s, 25, "bf16", "cuda", 1.0)
+    dout, _, _ = si.device_qkv(si.Shape(1, 2, 8, 1, d, d), 26, "bf16", "cuda", 1.0)
+    scale = default_scale(d)
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dout, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(0, 1)]
+    ref = oracle_bwd_on(q, k, v, dout, True, scale, heads=heads)
+    got = tuple(torch.stack([g[b, h] for b, h in heads]) for g in (dq, dk, dv))
+    compare_grads(got, ref, "bf16", f"bwd Nk={s.Nk}")
