@@ -40,12 +40,13 @@
 //    blocks of one head whose causal costs add up to a constant, numbered
 //    so that workgroups of one XCD share heads (K/V reuse in that L2).
 //  * At d = 64 the kernel needs 80 KiB of LDS and about 125 registers, so
-//    two workgroups share a CU (the launch bounds ask for two there).  Their items start and end at different
-//    times, and one workgroup's item boundary (Q and first tiles in
-//    flight, output stores) overlaps the other's tile loop.  That wins
-//    over the one-workgroup ping-pong kernel of fa_fwd_mfma.hip while items
-//    are short (up to about 48 key tiles); the ping-pong's vector/matrix
-//    alternation wins on longer key ranges.
+//    two workgroups share a CU (the launch bounds ask for two there).
+//    Their items start and end at different times, and one workgroup's
+//    item boundary (Q and first tiles in flight, output stores) overlaps
+//    the other's tile loop.  That wins over the one-workgroup ping-pong
+//    kernel of fa_fwd_mfma.hip while items are short (up to about 48 key
+//    tiles); the ping-pong's vector/matrix alternation wins on longer key
+//    ranges.
 #include <type_traits>
 
 #include "fa_device.h"
