@@ -1,8 +1,8 @@
 // fa_fwd_mfma.hip -- exact attention forward on the CDNA4 matrix cores.
 //
-// bf16/fp16 inputs, (d, dv) in {(64, 64), (64, 128), (128, 64)}, scale > 0;
-// fp32 accumulation.  (d = dv = 128, and d = dv = 64 with at most 3072
-// keys, run on the two-workgroup variant in fa_fwd_mfma_wide.hip.)
+// bf16/fp16 inputs, (d, dv) in {(64, 64), (128, 64)}, scale > 0; fp32
+// accumulation.  (d = dv = 128, d = 64 with dv = 128, and d = dv = 64 with
+// at most 3072 keys run on the 32x32 variant in fa_fwd_mfma_wide.hip.)
 //
 // Method: the FlashAttention-2 loop order of CS349E Lecture 11
 // "flash_lab.py", section 3 (flash_fwd, order "fa2"): one block of 256
@@ -625,7 +625,6 @@ hipError_t launch2(const FwdArgs &a) {
 template <typename T>
 hipError_t launch1(const FwdArgs &a) {
     if (a.d == 64 && a.dv == 64) return launch2<T, 64, 64>(a);
-    if (a.d == 64 && a.dv == 128) return launch2<T, 64, 128>(a);
     if (a.d == 128 && a.dv == 64) return launch2<T, 128, 64>(a);
     return hipErrorInvalidValue;
 }

@@ -47,12 +47,12 @@ struct BwdArgs {
 hipError_t launch_fwd_rowwise(const FwdArgs &a);
 
 // MFMA forward for bf16/fp16 with d, dv in {64, 128} and scale > 0:
-// d = dv = 128, and d = dv = 64 over short key ranges, on the 32x32 kernel,
-// the other cases on the 16x16 ping-pong kernel.
+// d = dv = 128, d = 64 with dv = 128, and d = dv = 64 over short key ranges
+// on the 32x32 kernel; the other cases on the 16x16 ping-pong kernel.
 bool fwd_mfma_supported(int dtype, int64_t d, int64_t dv, float scale);
 hipError_t launch_fwd_mfma16(const FwdArgs &a);      // fa_fwd_mfma.hip
 // True where the 32x32 kernel of fa_fwd_mfma_wide.hip is the faster one:
-// d = dv = 128, and d = dv = 64 with Nk <= 3072.
+// d = dv = 128, d = 64 with dv = 128, and d = dv = 64 with Nk <= 3072.
 bool fwd_wide_preferred(int64_t d, int64_t dv, int64_t Nk);
 hipError_t launch_fwd_mfma_wide(const FwdArgs &a);   // fa_fwd_mfma_wide.hip
 // MFMA forward for every other bf16/fp16 case (any d, dv of 32..256, any
