@@ -655,7 +655,7 @@ def main() -> int:
                        "num_splits": wd.num_splits},
         },
         "roofline": {
-            "kernel": "fwd_mfma32_kernel<bf16,64,causal>",
+            "kernel": "fwd_mfma32_kernel<bf16,64,64,causal>",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
