@@ -4,7 +4,13 @@ One step = one pass of the whole path over one batch of synthetic inputs:
   1. fa_fwd on the GPT-2-medium-shaped prefill: B=64, H=16, N=Nk=1024,
      d=dv=64, bf16, causal (inputs 0.5*N(0,1));
   2. fa_decode_splitkv on the long-context decode: B=8, H=32, N=1,
-     Nk=32768, d=dv=128, bf16, 64 splits (segment kernel + merge kernel).
+     Nk=32768, d=dv=128, bf16, 64 splits (segment kernel + merge kernel);
+  3. fa_fwd on the long-sequence prefill: B=2, H=32, N=Nk=8192, d=dv=128,
+     bf16, causal (reported in its own sub-record).
+In this order each prefill launch follows at least 0.5 GB of other traffic
+(the decode streams 4.3 GB of K/V, the long prefill touches 0.5 GB), which
+is larger than every cache (L2 4 MB per XCD, MALL 256 MB): that traffic is
+the cache flush between prefill repetitions.
 
 Inputs are drawn on the GPU with seeded generators before timing starts.
 Every launch is bracketed by HIP events recorded on the stream the library
@@ -41,6 +47,11 @@ PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0          # HBM3E
 PREFILL = "prefill_b64_h16_n1024_d64"
 DECODE = "decode_b8_h32_nk32768_d128"
+LONG = "prefill_b2_h32_n8192_d128"
+# Kernel names (demangled template arguments) of the forward launches the
+# default step makes: bf16, (d, dv) = (64, 64) and (128, 128), causal.
+FWD_C3_NAME = "fwd_mfma32_kernelIDF16bLi64ELi64ELb1E"
+FWD_C4_NAME = "fwd_mfma32_kernelIDF16bLi128ELi128ELb1E"
 FWD_KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc",
                               "fa_fwd_mfma_wide.hip")
 DEC_KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc",
@@ -78,7 +89,7 @@ def source_hash(path: str) -> str:
 def read_traffic():
     """Per-launch HBM traffic from the committed counter summary, or None per
     kernel if absent or if that kernel's source changed since it was taken."""
-    out = {"fwd": None, "decode": None}
+    out = {"fwd": None, "decode": None, "long": None}
     if not os.path.exists(TRAFFIC_FILE):
         return out
     kv = {}
@@ -90,6 +101,8 @@ def read_traffic():
     try:
         if kv.get("fwd_source_sha256_16") == source_hash(FWD_KERNEL_SRC):
             out["fwd"] = float(kv["fwd_bytes_per_launch"])
+            if "long_bytes_per_launch" in kv:
+                out["long"] = float(kv["long_bytes_per_launch"])
         if kv.get("decode_source_sha256_16") == source_hash(DEC_KERNEL_SRC):
             out["decode"] = float(kv["decode_bytes_per_launch"])
     except (KeyError, ValueError):
@@ -115,6 +128,46 @@ def cpu_baseline(q, k, v, s, causal, heads: int):
             "cpu": cpu_model(),
             "sample": f"{heads} of {s.B * s.H} heads of {PREFILL} (FP64 standard attention, "
                       f"{flops / 1e9:.1f} GFLOP credited, {dt:.2f} s wall on {threads} threads)"}
+
+
+def gpu_clock():
+    """The GPU's shader-clock readings from amd-smi (current and maximum, MHz),
+    taken right after the timed region; None where the tool gives none.  The
+    peaks above assume 2.4 GHz."""
+    import subprocess
+    out = {}
+    for key, cmd in (("metric", ["amd-smi", "metric", "-g", "0", "--clock", "--json"]),
+                     ("static", ["amd-smi", "static", "-g", "0", "--clock", "--json"])):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            if r.returncode == 0:
+                out[key] = json.loads(r.stdout)
+        except (OSError, subprocess.SubprocessError, ValueError):
+            pass
+    return _clock_fields(out) if out else None
+
+
+def _clock_fields(raw):
+    """GFX clock figures (MHz) found in amd-smi's JSON, by key path."""
+    found = {}
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            for k2, v2 in x.items():
+                walk(v2, path + (str(k2),))
+        elif isinstance(x, list):
+            for i, v2 in enumerate(x):
+                walk(v2, path + (str(i),))
+        else:
+            p = "/".join(path).lower()
+            if ("gfx" in p or "sclk" in p) and ("clk" in p or "clock" in p):
+                try:
+                    found["/".join(path)] = float(x)
+                except (TypeError, ValueError):
+                    pass
+
+    walk(raw, ())
+    return found or None
 
 
 def cpu_model() -> str:
@@ -149,7 +202,8 @@ def summarize_pmc(directory: str) -> None:
         vals = values(counter, pred)
         return sum(vals) / len(vals) if vals else None
 
-    is_fwd = lambda n: "fwd_mfma32_kernel" in n
+    is_fwd = lambda n: FWD_C3_NAME in n
+    is_long = lambda n: FWD_C4_NAME in n
     is_seg = lambda n: "decode_segment_kernel" in n
     is_merge = lambda n: "decode_merge_kernel" in n
     # The 1 GiB calibration copy is a device-to-device memcpy; it is by far the
@@ -164,10 +218,13 @@ def summarize_pmc(directory: str) -> None:
         scale = COPY_BYTES / (cp * 1024.0)   # true bytes per counted byte
         out[counter] = {"copy_kib": cp, "scale": scale,
                         "fwd_kib": per_kernel(counter, is_fwd),
+                        "long_kib": per_kernel(counter, is_long),
                         "seg_kib": per_kernel(counter, is_seg),
                         "merge_kib": per_kernel(counter, is_merge)}
     fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
     fwd_b = (fetch["fwd_kib"] * 1024 * fetch["scale"] + write["fwd_kib"] * 1024 * write["scale"])
+    long_b = (fetch["long_kib"] * 1024 * fetch["scale"] + write["long_kib"] * 1024 * write["scale"]
+              if fetch["long_kib"] is not None and write["long_kib"] is not None else None)
     dec_b = ((fetch["seg_kib"] + fetch["merge_kib"]) * 1024 * fetch["scale"]
              + (write["seg_kib"] + write["merge_kib"]) * 1024 * write["scale"])
     lines = [
@@ -187,6 +244,9 @@ def summarize_pmc(directory: str) -> None:
         f"fwd_write_kib: {write['fwd_kib']:.1f}",
         f"fwd_bytes_per_launch: {fwd_b:.0f}",
         f"fwd_source_sha256_16: {source_hash(FWD_KERNEL_SRC)}",
+        *([f"long_fetch_kib: {fetch['long_kib']:.1f}",
+           f"long_write_kib: {write['long_kib']:.1f}",
+           f"long_bytes_per_launch: {long_b:.0f}"] if long_b is not None else []),
         f"decode_segment_fetch_kib: {fetch['seg_kib']:.1f}",
         f"decode_segment_write_kib: {write['seg_kib']:.1f}",
         f"decode_merge_fetch_kib: {fetch['merge_kib']:.1f}",
@@ -210,7 +270,7 @@ def summarize_trace(directory: str) -> None:
     rows = list(csv.DictReader(open(paths[0])))
     default_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- "
                    "python $R/bench.py --no-cpu-baseline   (run from /tmp, repo at $R; 50 timed + "
-                   "10 warm-up steps, each one fa_fwd and one fa_decode_splitkv call)")
+                   "10 warm-up steps, each two fa_fwd calls and one fa_decode_splitkv call)")
     gqa_cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_gqa -o run -- "
                "python $R/bench.py --only gqa   (run from /tmp, repo at $R; 50 timed + 10 warm-up "
                "fa_decode_splitkv_gqa calls)")
@@ -219,7 +279,8 @@ def summarize_trace(directory: str) -> None:
                "fa_bwd calls)")
     # file -> (kernel that must be in the trace, kernels listed, command)
     groups = {
-        f"fwd_mfma32_kernel_{PREFILL}.txt": ("fwd_mfma32_kernel", ("fwd_mfma32_kernel",), default_cmd),
+        f"fwd_mfma32_kernel_{PREFILL}.txt": (FWD_C3_NAME, (FWD_C3_NAME,), default_cmd),
+        f"fwd_mfma32_kernel_{LONG}.txt": (FWD_C4_NAME, (FWD_C4_NAME,), default_cmd),
         f"decode_splitkv_{DECODE}.txt": ("decode_segment_kernel",
                                          ("decode_segment_kernel", "decode_merge_kernel"),
                                          default_cmd),
@@ -530,7 +591,7 @@ def main() -> int:
                     help="prefill heads the CPU oracle is timed on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="add one plain 1 GiB device copy per step (for counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "gqa", "bwd", "dims"],
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "gqa", "bwd", "dims"],
                     help="profile one entry point alone (the JSON line then omits the other); "
                          "'gqa' times the grouped-query decode, 'bwd' the backward, 'dims' "
                          "other head dimensions (none of these is part of the default line)")
@@ -573,18 +634,26 @@ def main() -> int:
         return split_sweep(args, torch, fa)
     wp = si.WORKLOADS[PREFILL]
     wd = si.WORKLOADS[DECODE]
-    sp, sd = wp.shapes[0], wd.shapes[0]
-    print(f"# drawing inputs: {wp.description}; {wd.description}", file=sys.stderr, flush=True)
+    wl = si.WORKLOADS[LONG]
+    sp, sd, sl = wp.shapes[0], wd.shapes[0], wl.shapes[0]
+    print(f"# drawing inputs: {wp.description}; {wd.description}; {wl.description}",
+          file=sys.stderr, flush=True)
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
+    run_l = args.only in (None, "long")
     if not run_p:
         sp = si.Shape(1, 1, 1, 1, sp.d, sp.dv)
     if not run_d:
         sd = si.Shape(1, 1, 1, 1, sd.d, sd.dv)
+    if not run_l:
+        sl = si.Shape(1, 1, 1, 1, sl.d, sl.dv)
     qp, kp, vp = si.device_qkv(sp, wp.seed, wp.dtype, dev, wp.std)
     qd, kd, vd = si.device_qkv(sd, wd.seed, wd.dtype, dev, wd.std)
+    ql, kl, vl = si.device_qkv(sl, wl.seed, wl.dtype, dev, wl.std)
     op = torch.empty((sp.B, sp.H, sp.N, sp.dv), dtype=qp.dtype, device=dev)
     lp = torch.empty((sp.B, sp.H, sp.N), dtype=torch.float32, device=dev)
+    ol = torch.empty((sl.B, sl.H, sl.N, sl.dv), dtype=ql.dtype, device=dev)
+    ll = torch.empty((sl.B, sl.H, sl.N), dtype=torch.float32, device=dev)
     od = torch.empty((sd.B, sd.H, sd.N, sd.dv), dtype=qd.dtype, device=dev)
     ld = torch.empty((sd.B, sd.H, sd.N), dtype=torch.float32, device=dev)
     ws = torch.empty(fa.decode_splitkv_workspace_size(sd.B, sd.H, sd.N, sd.dv, wd.num_splits),
@@ -596,6 +665,7 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     scale_p = 1.0 / math.sqrt(sp.d)
     scale_d = 1.0 / math.sqrt(sd.d)
+    scale_l = 1.0 / math.sqrt(sl.d)
 
     def step(ev=None):
         if ev is not None:
@@ -609,13 +679,17 @@ def main() -> int:
                               workspace=ws, out=od, lse=ld)
         if ev is not None:
             ev[2].record(stream)
+        if run_l:
+            fa.fwd(ql, kl, vl, causal=True, scale=scale_l, out=ol, lse=ll)
+        if ev is not None:
+            ev[3].record(stream)
         if copy_src is not None:
             copy_dst.copy_(copy_src)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -624,7 +698,10 @@ def main() -> int:
     wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    long_ms = [e[2].elapsed_time(e[3]) for e in events]
     assert torch.isfinite(lp).all().item() and torch.isfinite(ld).all().item()
+    assert torch.isfinite(ll).all().item()
+    clock = gpu_clock()
 
     flops = credited_flops(sp, True)
     fwd_avg_s = sum(fwd_ms) / len(fwd_ms) / 1e3
@@ -633,6 +710,9 @@ def main() -> int:
     dbytes = decode_bytes(sd)
     dec_gbs = dbytes / dec_avg_s / 1e9
     traffic = read_traffic()
+    lflops = credited_flops(sl, True)
+    long_avg_s = sum(long_ms) / len(long_ms) / 1e3
+    ltflops = lflops / long_avg_s / 1e12
 
     result = {
         "metric": METRIC,
@@ -653,7 +733,10 @@ def main() -> int:
                         "input_std": wp.std},
             "decode": {"B": sd.B, "H": sd.H, "N": sd.N, "Nk": sd.Nk, "d": sd.d,
                        "num_splits": wd.num_splits},
+            "long_prefill": {"B": sl.B, "H": sl.H, "N": sl.N, "Nk": sl.Nk, "d": sl.d,
+                             "causal": True, "input_std": wl.std},
         },
+        "gpu_clock": clock,
         "roofline": {
             "kernel": "fwd_mfma32_kernel<bf16,64,64,causal>",
             "bound": "mfma",
@@ -685,6 +768,25 @@ def main() -> int:
                 "algorithmic_bytes_per_launch": dbytes,
             },
         },
+        "long_prefill": {
+            "metric": "attn fwd TFLOP/s (% bf16 MFMA peak), long causal prefill",
+            "workload": f"{LONG} (fa_fwd)",
+            "value": round(ltflops, 2),
+            "unit": "TFLOP/s",
+            "roofline": {
+                "kernel": "fwd_mfma32_kernel<bf16,128,128,causal>",
+                "bound": "mfma",
+                "achieved": round(ltflops, 2),
+                "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(ltflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic["long"],
+                "avg_launch_us": round(long_avg_s * 1e6, 2),
+                "median_launch_us": round(sorted(long_ms)[len(long_ms) // 2] * 1e3, 2),
+                "min_launch_us": round(min(long_ms) * 1e3, 2),
+                "credited_flop_per_launch": lflops,
+            },
+        },
         "cpu_baseline": None,
     }
     if not run_p:
@@ -692,6 +794,8 @@ def main() -> int:
         result["roofline"] = None
     if not run_d:
         result["decode"] = None
+    if not run_l:
+        result["long_prefill"] = None
     if not args.no_cpu_baseline and run_p:
         result["cpu_baseline"] = cpu_baseline(qp, kp, vp, sp, True, min(args.cpu_heads, sp.B * sp.H))
     print(json.dumps(result), flush=True)

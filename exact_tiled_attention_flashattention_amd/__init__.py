@@ -105,6 +105,32 @@ def _check_qkv(q, k, v, grouped=False):
     return B, H, N, k.shape[2], d, v.shape[3]
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output or operand tensor must match exactly: the C ABI
+    sees only a raw pointer, so a short, strided, mistyped or host tensor
+    would be written out of bounds instead of failing."""
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        got = (f"{tuple(t.shape)} {t.dtype} on {t.device}"
+               f"{'' if t.is_contiguous() else ', non-contiguous'}"
+               if isinstance(t, torch.Tensor) else type(t).__name__)
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}, got {got}")
+    return t
+
+
+def _check_workspace(t, nbytes, device):
+    """A caller-supplied workspace: a contiguous uint8 tensor on ``device`` of
+    at least ``nbytes`` bytes."""
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.device != device
+            or not t.is_contiguous() or t.numel() < nbytes):
+        got = (f"{t.numel()} {t.dtype} elements on {t.device}" if isinstance(t, torch.Tensor)
+               else type(t).__name__)
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} "
+                         f"bytes on {device}, got {got}")
+    return t
+
+
 def _stream_handle(device, stream):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -124,10 +150,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     B, H, N, Nk, d, dv = _check_qkv(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = (torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device) if out is None
+           else _check_buffer("out", out, (B, H, N, dv), q.dtype, q.device))
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _check_buffer("lse", lse, (B, H, N), torch.float32, q.device))
     st = library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           B, H, N, Nk, d, dv, int(bool(causal)), float(scale),
                           _DTYPE_CODE[q.dtype], _stream_handle(q.device, stream))
@@ -161,12 +187,14 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
                              f"on {q.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _check_buffer("dq", dq, q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_buffer("dk", dk, k.shape, q.dtype, q.device)
+    dv = torch.empty_like(v) if dv is None else _check_buffer("dv", dv, v.shape, q.dtype, q.device)
+    need = bwd_workspace_size(B, H, N)
     if workspace is None:
-        workspace = torch.empty(max(bwd_workspace_size(B, H, N), 16), dtype=torch.uint8,
-                                device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, need, q.device)
     st = library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                           B, H, N, Nk, d, dvd, int(bool(causal)), float(scale),
@@ -206,14 +234,18 @@ def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
     B, H, N, Nk, d, dv = _check_qkv(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    out = (torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device) if out is None
+           else _check_buffer("out", out, (B, H, N, dv), q.dtype, q.device))
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _check_buffer("lse", lse, (B, H, N), torch.float32, q.device))
+    if num_splits < 0:
+        raise ValueError(f"num_splits must be >= 0, got {num_splits}")
+    splits = num_splits or decode_splitkv_auto_splits(B, H, H, N, Nk, d, dv, q.dtype)
+    nbytes = decode_splitkv_workspace_size(B, H, N, dv, splits)
     if workspace is None:
-        splits = num_splits or decode_splitkv_auto_splits(B, H, H, N, Nk, d, dv, q.dtype)
-        nbytes = decode_splitkv_workspace_size(B, H, N, dv, splits)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, nbytes, q.device)
     st = library().fa_decode_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                      lse.data_ptr(), B, H, N, Nk, d, dv, int(bool(causal)),
                                      float(scale), _DTYPE_CODE[q.dtype], int(num_splits),
@@ -237,14 +269,18 @@ def decode_splitkv_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     B, Hq, Hkv, N, Nk, d, dv = _check_qkv(q, k, v, grouped=True)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    out = (torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device) if out is None
+           else _check_buffer("out", out, (B, Hq, N, dv), q.dtype, q.device))
+    lse = (torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None
+           else _check_buffer("lse", lse, (B, Hq, N), torch.float32, q.device))
+    if num_splits < 0:
+        raise ValueError(f"num_splits must be >= 0, got {num_splits}")
+    splits = num_splits or decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dv, q.dtype)
+    nbytes = decode_splitkv_workspace_size(B, Hq, N, dv, splits)
     if workspace is None:
-        splits = num_splits or decode_splitkv_auto_splits(B, Hq, Hkv, N, Nk, d, dv, q.dtype)
-        nbytes = decode_splitkv_workspace_size(B, Hq, N, dv, splits)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, nbytes, q.device)
     st = library().fa_decode_splitkv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          lse.data_ptr(), B, Hq, Hkv, N, Nk, d, dv,
                                          int(bool(causal)), float(scale), _DTYPE_CODE[q.dtype],

@@ -141,10 +141,13 @@ fa_status_t fa_fwd(const void *q, const void *k, const void *v, void *o, float *
 size_t fa_decode_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t dv,
                                         int num_splits) {
     if (B < 1 || H < 1 || N < 1 || dv < 1 || num_splits < 1) return 0;
-    int64_t x;
-    if (!mul_ok(B, H, &x) || !mul_ok(x, num_splits, &x) || !mul_ok(x, N, &x) ||
-        !mul_ok(x, dv + 1, &x) || !mul_ok(x, 4, &x))
+    // rows = B H S N; bytes = rows (dv + 1) 4, formed without signed overflow
+    int64_t rows, x;
+    if (!mul_ok(B, H, &rows) || !mul_ok(rows, num_splits, &rows) || !mul_ok(rows, N, &rows) ||
+        !mul_ok(rows, dv, &x) || x > std::numeric_limits<int64_t>::max() - rows)
         return 0;
+    x += rows;
+    if (!mul_ok(x, 4, &x)) return 0;
     if ((uint64_t)x > (uint64_t)std::numeric_limits<size_t>::max()) return 0;
     return static_cast<size_t>(x);
 }

@@ -2,7 +2,7 @@
 // (any dtype) gradient kernels, plus the launcher that picks them or the
 // matrix-core kernels of fa_bwd_mfma.hip.
 //
-// Method: CS349E Lecture 11 "flash_lab.py", section 5 (flash_bwd, the
+// Method: CS349E Lecture 11 "flash_lab.py", section 3 (flash_bwd, the
 // FlashAttention-2 backward): the N x Nk probabilities are not stored by the
 // forward; they are recomputed on chip from Q, K and the forward's LSE as
 // P_ij = exp(S_ij - LSE_i).  With D_i = sum_c dO_ic O_ic (one number per

@@ -1,7 +1,7 @@
 // fa_bwd_mfma.hip -- attention backward on the CDNA4 matrix cores
 // (bf16/fp16 inputs, d and dv in {32, 64, 128, 256}, fp32 accumulation).
 //
-// Method: CS349E Lecture 11 "flash_lab.py", section 5 (flash_bwd, the
+// Method: CS349E Lecture 11 "flash_lab.py", section 3 (flash_bwd, the
 // FlashAttention-2 backward).  The probabilities are recomputed from Q, K
 // and the forward's LSE, P = exp(S - LSE) (here exp2 of S scale log2(e) -
 // LSE log2(e)); with D_i = rowsum(dO o O) (computed by the dQ kernel, which

@@ -199,13 +199,13 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
 
 /*
  * fa_bwd -- gradients of exact attention (the FlashAttention-2 backward of
- * flash_lab.py section 5, flash_bwd): given the forward's inputs, its outputs
+ * flash_lab.py section 3, flash_bwd): given the forward's inputs, its outputs
  * o and lse (as fa_fwd writes them) and the output gradient dout, writes
  *     dq = dL/dq, dk = dL/dk, dv = dL/dv   for L = sum(dout * O),
  * i.e. with P = exp(S - LSE) recomputed from q, k and lse (never stored),
  *     D_i = sum_c dout_ic o_ic,  dv = P^T dout,  dP = dout v^T,
  *     dS = P * (dP - D),  dq = scale dS k,  dk = scale dS^T q,
- * the gradients section 5's standard_attention_bwd defines.  Rows that see
+ * the gradients section 2's standard_attention_bwd defines.  Rows that see
  * no key (lse = -inf) contribute nothing; keys no row sees get dk = dv = 0.
  *
  *   q, k, v, causal, scale, dtype, sizes   as for fa_fwd (the same call).

@@ -13,7 +13,7 @@
  *                                 merge_states
  *           §2 standard attention -- _causal_mask, standard_attention
  *           §4 flash-decoding  -- split_kv_decode
- *           §5 backward        -- standard_attention_bwd
+ *           §2 backward of standard attention -- standard_attention_bwd
  *   [FF]  CS349E Lecture 11 "02_flash_forward.py", demo 1 (correctness): the
  *         flash forward computes exactly the standard result.
  *
@@ -378,7 +378,7 @@ int oracle_split_kv_decode(const double *q, const double *K, const double *V,
 }
 
 /* ------------------------------------------------------------------------ */
-/* [FL] §5 standard attention backward, one head, from the materialised P    */
+/* [FL] §2 standard attention backward, one head, from the materialised P    */
 /* of the forward definition above (a row with no visible key has P = 0):    */
 /*   D_i   = sum_c dO_ic O_ic                                                */
 /*   dV    = P^T dO                                                          */

@@ -11,7 +11,7 @@ Run as ``python -m tests.oracle_pins <liboracle.so>`` to print the names of the
 failing pins as JSON (used by the mutant test, one subprocess per build).
 
 Citations name the page and section: [FL] = CS349E Lecture 11 shared module
-flash_lab.py (section 5 is the backward); [XS] = xserv design doc
+flash_lab.py (section 2 holds the backward of standard attention); [XS] = xserv design doc
 "04-transformer-kernels", test plan.
 """
 from __future__ import annotations
@@ -404,7 +404,7 @@ def pin_split_kv_decode(orc):
 
 
 # --------------------------------------------------------------------------
-# pins of the backward ([FL] section 5, standard_attention_bwd)
+# pins of the backward ([FL] section 2, standard_attention_bwd)
 # --------------------------------------------------------------------------
 def _loss(orc, q, k, v, dout, causal, scale):
     """sum(dout * O): the scalar whose gradient the backward returns."""

@@ -106,19 +106,26 @@ def default_scale(d):
     return 1.0 / math.sqrt(d)
 
 
-def score_scaled_tolerance(q, k, v, scale, dtype: str):
+def score_scaled_tolerance(q, k, v, scale, dtype: str, causal: bool):
     """Tolerance for inputs whose scores are far larger than the workloads'.
 
-    A float32 score is a sum of d products; its rounding error grows with
-    the magnitudes summed, about a few units of 2^-24 times
-    s_abs = |scale| * max_ij sum_c |q_ic k_jc|.  A score error e perturbs
-    every weight exp(score) by a relative e, so O moves by up to
-    2 e max|v| (numerator and denominator) and LSE by e.  The bar is the
-    dtype's bar plus that bound with e = 8 * 2^-24 * s_abs."""
-    qa = np.abs(si.as_f64(q))
-    ka = np.abs(si.as_f64(k))
-    va = si.as_f64(v)
-    s_abs = float(np.max(qa @ np.swapaxes(ka, -1, -2))) * abs(scale)
-    e = 8 * 2.0 ** -24 * s_abs
+    First-order perturbation bound.  If every score s_ij carries an error
+    e_ij, the softmax weights move to p_ij (1 + e_ij - sum_k p_ik e_ik), so
+        |dO_ic|  <= sum_j p_ij |e_ij| |v_jc - O_ic|,
+        |dLSE_i| <= sum_j p_ij |e_ij|.
+    A float32 score is a length-d inner product; its rounding error is
+    bounded, in the probabilistic sense of Higham and Mary's analysis, by
+    sqrt(d) * 2^-24 * |scale| * sum_c |q_ic k_jc|.  The bar is the dtype's
+    bar plus that bound, evaluated with the oracle's P on these inputs: weights
+    of keys that hardly count, and keys whose value rows equal the output,
+    add nothing, unlike the worst case over all keys."""
+    qf, kf, vf = si.as_f64(q), si.as_f64(k), si.as_f64(v)
+    d = qf.shape[-1]
+    o_ref, _, p = oracle.attention(qf, kf, vf, causal=causal, scale=scale, want_p=True)
+    eps = math.sqrt(d) * 2.0 ** -24 * abs(scale) * (np.abs(qf) @ np.swapaxes(np.abs(kf), -1, -2))
+    w = p * eps                                              # [..., N, Nk]
+    dev = np.abs(vf[..., None, :, :] - o_ref[..., :, None, :])   # [..., N, Nk, dv]
+    bound_o = float(np.max(np.einsum("...ij,...ijc->...ic", w, dev)))
+    bound_l = float(np.max(w.sum(-1)))
     base_o, base_l = TOL[dtype]
-    return base_o + 2 * e * float(np.abs(va).max()), base_l + e
+    return base_o + bound_o, base_l + bound_l

@@ -239,3 +239,48 @@ def test_binding_requires_gpu_tensors():
         fa.decode_splitkv_gqa(x, x, x)
     with pytest.raises(ValueError):
         fa.bwd(x, x, x, x, torch.zeros(1, 1, 4), x)
+
+
+# ---- caller-supplied outputs and workspace (binding checks, no launch) ------
+
+_DEV = torch.device("cpu")
+
+
+@pytest.mark.parametrize("t,why", [
+    (torch.empty(2, 3, 5, 64, dtype=torch.bfloat16), "right"),
+    (torch.empty(2, 3, 4, 64, dtype=torch.bfloat16), "shape"),
+    (torch.empty(2, 3, 5, 64, dtype=torch.float16), "dtype"),
+    (torch.empty(2, 3, 64, 5, dtype=torch.bfloat16).transpose(2, 3), "strides"),
+    (torch.empty(2 * 3 * 5 * 64, dtype=torch.bfloat16), "flat"),
+    (None, "not a tensor"),
+])
+def test_binding_checks_supplied_outputs(t, why):
+    """A supplied o / lse / dq / dk / dv must match exactly (shape, dtype,
+    device, contiguity); the C ABI sees only its address."""
+    shape, dtype = (2, 3, 5, 64), torch.bfloat16
+    if why == "right":
+        assert fa._check_buffer("out", t, shape, dtype, _DEV) is t
+        return
+    with pytest.raises(ValueError, match="out must be a contiguous"):
+        fa._check_buffer("out", t, shape, dtype, _DEV)
+
+
+def test_binding_checks_supplied_output_device():
+    t = torch.empty(1, 1, 4, dtype=torch.float32, device="meta")
+    with pytest.raises(ValueError, match="lse must be a contiguous"):
+        fa._check_buffer("lse", t, (1, 1, 4), torch.float32, _DEV)
+
+
+@pytest.mark.parametrize("t,ok", [
+    (torch.empty(1000, dtype=torch.uint8), True),
+    (torch.empty(999, dtype=torch.uint8), False),          # too small
+    (torch.empty(250, dtype=torch.float32), False),        # 1000 bytes, wrong dtype
+    (torch.empty(2000, dtype=torch.uint8)[::2], False),    # strided
+    (torch.empty(1000, dtype=torch.uint8, device="meta"), False),
+])
+def test_binding_checks_supplied_workspace(t, ok):
+    if ok:
+        assert fa._check_workspace(t, 1000, _DEV) is t
+    else:
+        with pytest.raises(ValueError, match="workspace must be"):
+            fa._check_workspace(t, 1000, _DEV)

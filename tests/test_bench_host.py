@@ -42,6 +42,7 @@ def _traffic_file(tmp_path, fwd_hash, dec_hash):
     p.write_text("# test\n"
                  "fwd_bytes_per_launch: 1000\n"
                  f"fwd_source_sha256_16: {fwd_hash}\n"
+                 "long_bytes_per_launch: 3000\n"
                  "decode_bytes_per_launch: 2000\n"
                  f"decode_source_sha256_16: {dec_hash}\n")
     return str(p)
@@ -51,18 +52,18 @@ def test_traffic_kept_while_sources_match(tmp_path, monkeypatch):
     path = _traffic_file(tmp_path, bench.source_hash(bench.FWD_KERNEL_SRC),
                          bench.source_hash(bench.DEC_KERNEL_SRC))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
-    assert bench.read_traffic() == {"fwd": 1000.0, "decode": 2000.0}
+    assert bench.read_traffic() == {"fwd": 1000.0, "decode": 2000.0, "long": 3000.0}
 
 
 def test_traffic_dropped_for_changed_source(tmp_path, monkeypatch):
     path = _traffic_file(tmp_path, "0" * 16, bench.source_hash(bench.DEC_KERNEL_SRC))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
-    assert bench.read_traffic() == {"fwd": None, "decode": 2000.0}
+    assert bench.read_traffic() == {"fwd": None, "decode": 2000.0, "long": None}
 
 
 def test_traffic_absent(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
-    assert bench.read_traffic() == {"fwd": None, "decode": None}
+    assert bench.read_traffic() == {"fwd": None, "decode": None, "long": None}
 
 
 @pytest.mark.parametrize("text", ["model name\t: Test CPU 9000\nflags\t: x\n", "flags\t: x\n"])
@@ -76,3 +77,17 @@ def test_cpu_model(tmp_path, monkeypatch, text):
 
     monkeypatch.setattr("builtins.open", fake_open)
     assert bench.cpu_model() == ("Test CPU 9000" if "model name" in text else "unknown")
+
+
+def test_credited_long_prefill_flops():
+    # 1.0995 TFLOP at B2 x H32 x 8192 x 8192, d = 128, causal.
+    s = si.Shape(2, 32, 8192, 8192, 128, 128)
+    assert bench.credited_flops(s, True) == 2 * 32 * 4.0 * 8192 * 8192 * 128 / 2
+
+
+def test_clock_fields_from_amd_smi_json():
+    raw = {"metric": [{"gpu": 0, "clock": {"gfx_0": {"clk": 2400, "min_clk": 500},
+                                           "mem_0": {"clk": 1900}}}]}
+    f = bench._clock_fields(raw)
+    assert f == {"metric/0/clock/gfx_0/clk": 2400.0, "metric/0/clock/gfx_0/min_clk": 500.0}
+    assert bench._clock_fields({"x": 1}) is None
