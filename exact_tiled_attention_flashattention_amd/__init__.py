@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = [
-    "fwd", "decode_splitkv", "decode_splitkv_gqa", "decode_splitkv_workspace_size",
+    "fwd", "decode_splitkv", "decode_splitkv_gqa", "decode_splitkv_noalloc",
+    "decode_splitkv_workspace_size", "DECODE_NOALLOC_MAX_WORKSPACE",
     "decode_splitkv_auto_splits", "bwd", "bwd_workspace_size", "status_string",
     "FAError", "library", "LIBRARY_PATH", "FA_OK", "FA_ERR_INVALID_ARG",
     "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_LAUNCH",
@@ -27,6 +28,9 @@ LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.s
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = range(5)
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+# FA_DECODE_NOALLOC_MAX_WORKSPACE of include/fa.h: the static scratch of
+# fa_decode_splitkv_noalloc, in bytes.
+DECODE_NOALLOC_MAX_WORKSPACE = 16 << 20
 
 _lib = None
 
@@ -58,6 +62,9 @@ def library() -> ctypes.CDLL:
     lib.fa_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, c_int,
                                       ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t, vp]
     lib.fa_decode_splitkv.restype = c_int
+    lib.fa_decode_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                              c_int, ctypes.c_float, c_int, c_int, vp]
+    lib.fa_decode_splitkv_noalloc.restype = c_int
     lib.fa_decode_splitkv_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                           c_int, ctypes.c_float, c_int, c_int, vp, ctypes.c_size_t,
                                           vp]
@@ -253,6 +260,33 @@ def decode_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
                                      _stream_handle(q.device, stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_splitkv")
+    return out, lse
+
+
+def decode_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           causal: bool = False, scale: float | None = None,
+                           num_splits: int = 64, out: torch.Tensor | None = None,
+                           lse: torch.Tensor | None = None,
+                           stream: torch.cuda.Stream | None = None):
+    """Split-KV flash-decoding through ``fa_decode_splitkv_noalloc``: the
+    result of :func:`decode_splitkv`, with the per-segment partials in the
+    library's static per-GPU scratch (``DECODE_NOALLOC_MAX_WORKSPACE`` bytes)
+    instead of a workspace; the library allocates nothing.  Calls that
+    overlap on one GPU race.  Pass ``out`` and ``lse`` to allocate nothing
+    here either."""
+    B, H, N, Nk, d, dv = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = (torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device) if out is None
+           else _check_buffer("out", out, (B, H, N, dv), q.dtype, q.device))
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _check_buffer("lse", lse, (B, H, N), torch.float32, q.device))
+    st = library().fa_decode_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             out.data_ptr(), lse.data_ptr(), B, H, N, Nk, d, dv,
+                                             int(bool(causal)), float(scale), _DTYPE_CODE[q.dtype],
+                                             int(num_splits), _stream_handle(q.device, stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_splitkv_noalloc")
     return out, lse
 
 

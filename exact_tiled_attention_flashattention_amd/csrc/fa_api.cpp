@@ -156,10 +156,15 @@ size_t fa_decode_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t
 
 namespace {
 
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_MAX_WORKSPACE, "scratch size");
+
+// use_scratch: the partials go to the device's static scratch (the
+// allocation-free entry point) instead of `workspace`.
 fa_status_t decode_impl(const void *q, const void *k, const void *v, void *o, float *lse,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t Nk, int64_t d,
                         int64_t dv, int causal, float scale, fa_dtype_t dtype, int num_splits,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+                        void *workspace, size_t workspace_bytes, void *stream,
+                        bool use_scratch = false) {
     if (num_splits < 0) return FA_ERR_INVALID_ARG;
     if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
     fa_status_t st = check_common(q, k, v, o, lse, B, Hq, N, Nk, d, dv, scale, dtype);
@@ -172,7 +177,12 @@ fa_status_t decode_impl(const void *q, const void *k, const void *v, void *o, fl
         return FA_ERR_UNSUPPORTED;
     const size_t need = fa_decode_splitkv_workspace_size(B, Hq, N, dv, num_splits);
     if (need == 0) return FA_ERR_INVALID_ARG;
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    if (use_scratch) {
+        if (need > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+    } else if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) {
+        return FA_ERR_WORKSPACE;
+    }
+    if (use_scratch && fa::decode_scratch(&workspace) != hipSuccess) return FA_ERR_LAUNCH;
     fa::DecodeArgs dargs;
     dargs.a = make_args(q, k, v, o, lse, B, Hq, N, Nk, d, dv, causal, scale, dtype, stream);
     dargs.Hkv = Hkv;
@@ -196,6 +206,14 @@ fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void 
                               void *stream) {
     return decode_impl(q, k, v, o, lse, B, H, H, N, Nk, d, dv, causal, scale, dtype, num_splits,
                        workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_splitkv_noalloc(const void *q, const void *k, const void *v, void *o,
+                                      float *lse, int64_t B, int64_t H, int64_t N, int64_t Nk,
+                                      int64_t d, int64_t dv, int causal, float scale,
+                                      fa_dtype_t dtype, int num_splits, void *stream) {
+    return decode_impl(q, k, v, o, lse, B, H, H, N, Nk, d, dv, causal, scale, dtype, num_splits,
+                       nullptr, 0, stream, true);
 }
 
 fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, void *o,

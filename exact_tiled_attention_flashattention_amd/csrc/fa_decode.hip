@@ -30,6 +30,8 @@
 // through LDS with the same merge rule.  The loop issues U loads of K and
 // U of V per lane before using them, to keep enough bytes in flight for
 // HBM bandwidth.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -387,6 +389,38 @@ hipError_t launch_decode_splitkv(const DecodeArgs &d) {
         case kBF16: return launch_typed<bf16_t>(d);
         default: return hipErrorInvalidValue;
     }
+}
+
+// ---- scratch of the allocation-free entry point ----------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops), the segment partials go to this fixed array instead
+// of a caller's workspace.  Each device holds its own copy from module load
+// until the process ends.  In host code the name `scratch` is only a host
+// stand-in, so its device address is looked up once per device, with that
+// device current, and only that address is ever passed to a kernel.  Every
+// call on a device shares the array: calls that overlap on one device race.
+// No part of it needs clearing: the segment kernels write every partial the
+// merge kernel reads (empty segments as lse = -inf, o = 0).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace fa

@@ -61,6 +61,12 @@ hipError_t launch_fwd_mfma_generic(const FwdArgs &a);
 
 // Split-KV decode: segment kernel then merge kernel, same stream.
 hipError_t launch_decode_splitkv(const DecodeArgs &a);
+// The per-device static scratch that the allocation-free decode entry point
+// uses as its workspace (fa_decode.hip): kDecodeScratchBytes bytes, 256-byte
+// aligned.  *ptr receives the current device's address of it (looked up
+// once per device with hipGetSymbolAddress, then cached).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void **ptr);
 // Matrix-core segment kernel (bf16/fp16), fa_decode_mfma.hip; it serves
 // kDecodeMfmaRows query rows per workgroup.
 constexpr int kDecodeMfmaRows = 16;

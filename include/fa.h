@@ -144,6 +144,36 @@ fa_status_t fa_decode_splitkv(const void *q, const void *k, const void *v, void 
                               void *stream);
 
 /*
+ * fa_decode_splitkv_noalloc -- fa_decode_splitkv without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The per-segment partials go to a static device array of
+ * FA_DECODE_NOALLOC_MAX_WORKSPACE bytes inside the library (one per GPU,
+ * held from library load until the process ends); the call allocates
+ * nothing.  Same kernels and result as fa_decode_splitkv with a workspace.
+ *
+ *   all arguments   as for fa_decode_splitkv (num_splits = 0 selects the
+ *                   automatic count).
+ * The workspace this shape would need,
+ * fa_decode_splitkv_workspace_size(B, H, N, dv, num_splits), must not
+ * exceed FA_DECODE_NOALLOC_MAX_WORKSPACE, else FA_ERR_WORKSPACE (nothing is
+ * launched).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on different streams, or from several threads) race
+ * and give undefined results; calls serialised on one stream are safe.  The
+ * array needs no clearing between calls: every partial the merge reads is
+ * written by the same call.  The first call on a device looks up the array's
+ * address on that device (the device must be current); failure there is
+ * FA_ERR_LAUNCH.
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE or
+ * FA_ERR_LAUNCH.
+ */
+#define FA_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+fa_status_t fa_decode_splitkv_noalloc(const void *q, const void *k, const void *v, void *o,
+                                      float *lse, int64_t B, int64_t H, int64_t N, int64_t Nk,
+                                      int64_t d, int64_t dv, int causal, float scale,
+                                      fa_dtype_t dtype, int num_splits, void *stream);
+
+/*
  * fa_decode_splitkv_gqa -- fa_decode_splitkv for grouped-query attention: Hq
  * query heads share Hkv key/value heads (Hq a multiple of Hkv), query head h
  * attending with key/value head h / (Hq / Hkv).  The result is that of

@@ -126,6 +126,22 @@ void test_decode() {
                                         FA_DTYPE_BF16) == 0);
 }
 
+void test_decode_noalloc() {
+    const int before = stub::last.calls;
+    // partials of 8 x 64 heads x 128 splits x 129 floats: 33.8 MB > 16 MiB
+    CHECK(fa_decode_splitkv_noalloc(P, P, P, P, L, 8, 64, 1, 32768, 128, 128, 0, 0.1f,
+                                    FA_DTYPE_BF16, 128, nullptr) == FA_ERR_WORKSPACE);
+    CHECK(fa_decode_splitkv_noalloc(nullptr, P, P, P, L, 8, 32, 1, 32768, 128, 128, 0, 0.1f,
+                                    FA_DTYPE_BF16, 64, nullptr) == FA_ERR_INVALID_ARG);
+    CHECK(stub::last.calls == before);
+    CHECK(fa_decode_splitkv_noalloc(P, P, P, P, L, 8, 32, 1, 32768, 128, 128, 0, 0.1f,
+                                    FA_DTYPE_BF16, 64, nullptr) == FA_OK);
+    const fa::DecodeArgs &d = stub::last.dec;
+    float *const s = reinterpret_cast<float *>(uintptr_t(0x800000));
+    CHECK(d.ws_o == s && d.ws_lse == s + int64_t(8) * 32 * 64 * 128 && d.num_splits == 64);
+    CHECK(fa_decode_splitkv_workspace_size(8, 32, 1, 128, 64) <= FA_DECODE_NOALLOC_MAX_WORKSPACE);
+}
+
 void test_bwd() {
     const size_t ws = fa_bwd_workspace_size(4, 8, 300);
     CHECK(ws == size_t(4) * 8 * 300 * 4);
@@ -153,6 +169,7 @@ void test_status_strings() {
 int main() {
     test_fwd();
     test_decode();
+    test_decode_noalloc();
     test_bwd();
     test_status_strings();
     if (failures) {

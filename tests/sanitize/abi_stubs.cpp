@@ -50,6 +50,13 @@ int64_t decode_workgroups_per_split(int dtype, int64_t d, int64_t dv, int64_t B,
     return B * Hkv * ((rows + r - 1) / r);
 }
 
+// A fake, 256-byte aligned address standing in for the static scratch.
+hipError_t decode_scratch(void **ptr) {
+    *ptr = reinterpret_cast<void *>(uintptr_t(0x800000));
+    stub::last.scratch_lookups += 1;
+    return hipSuccess;
+}
+
 hipError_t launch_bwd(const BwdArgs &b) {
     (void)record("bwd", b.a);
     stub::last.bwd = b;

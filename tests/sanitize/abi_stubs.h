@@ -7,6 +7,7 @@ namespace stub {
 struct Record {
     const char *kernel = nullptr;
     int calls = 0;
+    int scratch_lookups = 0;
     fa::FwdArgs fwd{};
     fa::DecodeArgs dec{};
     fa::BwdArgs bwd{};

@@ -28,7 +28,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode_splitkv",
                                      "fa_decode_splitkv_auto_splits",
-                                     "fa_decode_splitkv_gqa",
+                                     "fa_decode_splitkv_gqa", "fa_decode_splitkv_noalloc",
                                      "fa_decode_splitkv_workspace_size", "fa_fwd",
                                      "fa_status_string"]
 
@@ -284,3 +284,32 @@ def test_binding_checks_supplied_workspace(t, ok):
     else:
         with pytest.raises(ValueError, match="workspace must be"):
             fa._check_workspace(t, 1000, _DEV)
+
+
+def _noalloc(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=1, Nk=64, d=64, dv=64, causal=0,
+             scale=0.125, dtype=2, num_splits=4):
+    return fa.library().fa_decode_splitkv_noalloc(q, k, v, o, lse, B, H, N, Nk, d, dv, causal,
+                                                   scale, dtype, num_splits, None)
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_DECODE_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.DECODE_NOALLOC_MAX_WORKSPACE
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(num_splits=70000), fa.FA_ERR_UNSUPPORTED),
+    # the decode workload with 64 splits needs 8,454,144 bytes (fits); twice
+    # the heads and splits need 4x that, beyond the 16 MiB scratch
+    (dict(B=8, H=64, Nk=32768, d=128, dv=128, num_splits=128), fa.FA_ERR_WORKSPACE),
+    (dict(B=1, H=1, N=1, Nk=1 << 20, d=64, dv=64, num_splits=65536), fa.FA_ERR_WORKSPACE),
+])
+def test_noalloc_rejects(kw, expect):
+    """Invalid calls and shapes whose partials exceed the static scratch are
+    rejected before any HIP call."""
+    assert _noalloc(**kw) == expect
