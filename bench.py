@@ -130,44 +130,25 @@ def cpu_baseline(q, k, v, s, causal, heads: int):
                       f"{flops / 1e9:.1f} GFLOP credited, {dt:.2f} s wall on {threads} threads)"}
 
 
-def gpu_clock():
-    """The GPU's shader-clock readings from amd-smi (current and maximum, MHz),
-    taken right after the timed region; None where the tool gives none.  The
-    peaks above assume 2.4 GHz."""
-    import subprocess
-    out = {}
-    for key, cmd in (("metric", ["amd-smi", "metric", "-g", "0", "--clock", "--json"]),
-                     ("static", ["amd-smi", "static", "-g", "0", "--clock", "--json"])):
+def sclk_files():
+    """The DPM shader-clock tables of the amdgpu devices (sysfs pp_dpm_sclk)."""
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+
+def read_sclk(paths):
+    """Current shader clock (MHz) of each DPM table: the level marked '*'."""
+    out = []
+    for p in paths:
         try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-            if r.returncode == 0:
-                out[key] = json.loads(r.stdout)
-        except (OSError, subprocess.SubprocessError, ValueError):
+            with open(p) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        mhz = line.split(":", 1)[1].strip().rstrip("*").strip()
+                        out.append(float(mhz.lower().replace("mhz", "").strip()))
+                        break
+        except (OSError, ValueError, IndexError):
             pass
-    return _clock_fields(out) if out else None
-
-
-def _clock_fields(raw):
-    """GFX clock figures (MHz) found in amd-smi's JSON, by key path."""
-    found = {}
-
-    def walk(x, path):
-        if isinstance(x, dict):
-            for k2, v2 in x.items():
-                walk(v2, path + (str(k2),))
-        elif isinstance(x, list):
-            for i, v2 in enumerate(x):
-                walk(v2, path + (str(i),))
-        else:
-            p = "/".join(path).lower()
-            if ("gfx" in p or "sclk" in p) and ("clk" in p or "clock" in p):
-                try:
-                    found["/".join(path)] = float(x)
-                except (TypeError, ValueError):
-                    pass
-
-    walk(raw, ())
-    return found or None
+    return out
 
 
 def cpu_model() -> str:
@@ -691,9 +672,13 @@ def main() -> int:
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    sclk_paths = sclk_files()
+    sclk = []
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
+        if i % 4 == 3:
+            sclk += read_sclk(sclk_paths)   # while the queued steps run
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
@@ -701,7 +686,9 @@ def main() -> int:
     long_ms = [e[2].elapsed_time(e[3]) for e in events]
     assert torch.isfinite(lp).all().item() and torch.isfinite(ld).all().item()
     assert torch.isfinite(ll).all().item()
-    clock = gpu_clock()
+    clock = ({"sclk_mhz_during_timed_steps": sclk, "source": "sysfs pp_dpm_sclk (level "
+              "marked current), read by the host while the queued timed steps ran"}
+             if sclk else None)
 
     flops = credited_flops(sp, True)
     fwd_avg_s = sum(fwd_ms) / len(fwd_ms) / 1e3

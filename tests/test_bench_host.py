@@ -85,9 +85,10 @@ def test_credited_long_prefill_flops():
     assert bench.credited_flops(s, True) == 2 * 32 * 4.0 * 8192 * 8192 * 128 / 2
 
 
-def test_clock_fields_from_amd_smi_json():
-    raw = {"metric": [{"gpu": 0, "clock": {"gfx_0": {"clk": 2400, "min_clk": 500},
-                                           "mem_0": {"clk": 1900}}}]}
-    f = bench._clock_fields(raw)
-    assert f == {"metric/0/clock/gfx_0/clk": 2400.0, "metric/0/clock/gfx_0/min_clk": 500.0}
-    assert bench._clock_fields({"x": 1}) is None
+def test_read_sclk(tmp_path):
+    # the DPM table format: the current level carries a '*'
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text("0: 500Mhz \n1: 2317Mhz *\n2: 2400Mhz \n")
+    q = tmp_path / "other"
+    q.write_text("0: 500Mhz *\n1: 2400Mhz \n")
+    assert bench.read_sclk([str(p), str(q), str(tmp_path / "missing")]) == [2317.0, 500.0]
