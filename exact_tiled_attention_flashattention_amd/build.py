@@ -21,6 +21,12 @@ LIBRARY = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd_rowwise.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma_wide.hip", "fa_decode.hip",
            "fa_decode_mfma.hip", "fa_bwd.hip", "fa_bwd_mfma.hip",
            "fa_fwd_mfma_generic.hip"]
+# A second library, libfa_serial.so, differs only in fa_fwd_mfma_wide.hip,
+# built with FA_SERIAL_COPIES=1: every copy into LDS is waited for, between
+# barriers, before it is read.  Its results must equal libfa.so's bit for
+# bit (a race check of the staging); only the tests load it.
+SERIAL_SOURCE = "fa_fwd_mfma_wide.hip"
+SERIAL_LIBRARY = os.path.join(PKG, "libfa_serial.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -30,10 +36,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, serial: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", path, "-o", obj]
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ("_serial" if serial else "") + ".o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *(["-DFA_SERIAL_COPIES=1"] if serial else []), "-c",
+           path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON, "-x", "hip", "-c", path, "-o", obj] + DEVICE_FLAGS
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,15 +53,21 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = jobs or min(8, len(SOURCES))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIBRARY + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIBRARY)
-    if verbose:
-        print(f"built {LIBRARY}")
+        futs = [ex.submit(_compile, src) for src in SOURCES]
+        fut_serial = ex.submit(_compile, SERIAL_SOURCE, True)
+        objs = [f.result() for f in futs]
+        obj_serial = fut_serial.result()
+    serial_objs = [obj_serial if os.path.basename(o) == SERIAL_SOURCE.replace(".hip", ".o") else o
+                   for o in objs]
+    for lib, parts in ((LIBRARY, objs), (SERIAL_LIBRARY, serial_objs)):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"built {lib}")
     return LIBRARY
 
 

@@ -64,6 +64,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 // Eight waves; wave w owns query rows [32 w, 32 w + 32) of the block.
+// Checking build (FA_SERIAL_COPIES=1): every K/V tile and Q block is
+// copied between two barriers and waited for before anyone reads it, so no
+// copy is in flight while LDS is read.  The arithmetic and its order are
+// unchanged, so this build's results must equal the pipelined build's bit
+// for bit; only the race-check tests load it.
+#ifndef FA_SERIAL_COPIES
+#define FA_SERIAL_COPIES 0
+#endif
+constexpr bool kSerialCopies = FA_SERIAL_COPIES != 0;
+
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = 256;            // query rows per workgroup
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
     // over, its Q block already during the previous item; both are waited
     // for at the item's start (`pro_mark`).
     Cursor cur = first_item(sch);
-    if (cur.head >= 0) {
+    if (cur.head >= 0 && !kSerialCopies) {
         dma_q(cur.head, cur.qblk);
         first_tiles(cur.head, cur.ntiles);
     }
@@ -480,14 +490,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
         for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
         // The first tiles can only be fetched now that the previous item's
         // reads are over.
-        if (!first) {
+        if (!first && !kSerialCopies) {
             barrier();
             first_tiles(head, ntiles);
             pro_mark = issued;
         }
         first = false;
         // This item's Q block and first tiles have landed everywhere.
-        wait_pending(issued - pro_mark);
+        if (kSerialCopies) {
+            barrier();
+            dma_q(head, cur.qblk);
+            wait_pending(0);
+        } else {
+            wait_pending(issued - pro_mark);
+        }
         barrier();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -505,13 +521,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
             if (hd >= 0) dma_q(hd, qb);
             pro_mark = issued;
         };
-        if (ntiles == 0) {
+        if (ntiles == 0 && !kSerialCopies) {
             barrier();
             prefetch_next();
         }
         int mark = issued;
         // Iteration j: tile j sits in stage st = j % 3.
         auto sync = [&](const int j, const int st) __attribute__((always_inline)) {
+            if (kSerialCopies) {
+                barrier();
+                dma_k(head, j, st);
+                dma_v(head, j, st);
+                wait_pending(0);
+                barrier();
+                return;
+            }
             wait_pending(issued - mark);
             barrier();
             mark = issued;

@@ -70,6 +70,8 @@ void test_fwd() {
     CHECK(std::string_view(stub::last.kernel) == "fwd_mfma_wide");
     CHECK(stub::last.fwd.B == 64 && stub::last.fwd.H == 16 && stub::last.fwd.N == 1024 &&
           stub::last.fwd.causal == 1 && stub::last.fwd.scale == 0.125f);
+    CHECK(fwd(2, 32, 8192, 8192, 128, 128) == FA_OK);
+    CHECK(std::string_view(stub::last.kernel) == "fwd_mfma_wide");
     CHECK(fwd(1, 1, 5000, 5000, 64, 64) == FA_OK);
     CHECK(std::string_view(stub::last.kernel) == "fwd_mfma16");
     CHECK(fwd(1, 1, 50, 50, 32, 256) == FA_OK);
