@@ -20,7 +20,7 @@ LIBRARY = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd_rowwise.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma_wide.hip", "fa_decode.hip",
            "fa_decode_mfma.hip", "fa_bwd.hip", "fa_bwd_mfma.hip",
-           "fa_fwd_mfma_generic.hip"]
+           "fa_fwd_mfma_generic.hip", "fa_bwd_mfma32.hip"]
 # A second library, libfa_serial.so, differs only in fa_fwd_mfma_wide.hip,
 # built with FA_SERIAL_COPIES=1: every copy into LDS is waited for, between
 # barriers, before it is read.  Its results must equal libfa.so's bit for

@@ -228,7 +228,7 @@ fa_status_t fa_decode_splitkv_gqa(const void *q, const void *k, const void *v, v
 size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N) {
     if (B < 1 || H < 1 || N < 1) return 0;
     int64_t x;
-    if (!mul_ok(B, H, &x) || !mul_ok(x, N, &x) || !mul_ok(x, 4, &x)) return 0;
+    if (!mul_ok(B, H, &x) || !mul_ok(x, N, &x) || !mul_ok(x, 8, &x)) return 0;
     if ((uint64_t)x > (uint64_t)std::numeric_limits<size_t>::max()) return 0;
     return static_cast<size_t>(x);
 }

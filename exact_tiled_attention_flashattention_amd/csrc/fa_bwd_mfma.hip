@@ -193,8 +193,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
 
     const T *qh = q + (int64_t)head * N * D;
     const T *dh = dout + (int64_t)head * N * DV;
-    const float *Lh = lse + (int64_t)head * N;
-    const float *Dh = Dsum + (int64_t)head * N;
+    const float *Wh = Dsum + (int64_t)head * N * 2;   // (LSE log2 e, D) per row
     const auto qrs = make_rsrc(qh, (uint32_t)N * D * 2u);
     const auto drs = make_rsrc(dh, (uint32_t)N * DV * 2u);
     const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
@@ -275,11 +274,10 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
 
     // Steps are fetched two ahead: step x's data waits in register set x % 2
     // until it is stored to LDS stage x % 2 at the end of step x - 1.  The
-    // step's LSE and D are fetched the same way (bounds-checked: rows past N
-    // read 0; wave 0 stores them) and converted only when stored, so that
-    // nothing waits on the loads just issued.
-    const auto lrs = make_rsrc(Lh, (uint32_t)N * 4u);
-    const auto Drs = make_rsrc(Dh, (uint32_t)N * 4u);
+    // step's (LSE log2 e, D) pairs are fetched the same way (bounds-checked:
+    // rows past N read 0; wave 0 stores them), so that nothing waits on the
+    // loads just issued.
+    const auto wrs = make_rsrc(Wh, (uint32_t)N * 8u);
     u32x4 regs0[NL], regs1[NL];
     float vl0 = 0.f, vd0 = 0.f, vl1 = 0.f, vd1 = 0.f;
     auto load_step = [&](u32x4 (&rg)[NL], float &vl, float &vd, int s) {   // global -> registers
@@ -292,9 +290,9 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
             rg[t] = buffer_load16(isdo[t] ? drs : qrs, (isdo[t] ? baseo : baseq) + gofs[t]);
         // (every wave issues these two small loads, so that the count of
         // loads per step, and with it every wait, is the same on all paths)
-        const uint32_t off = (uint32_t)((s0 + s) * QS + lane % QS) * 4u;
-        vl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, (int)off, 0, 0));
-        vd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(Drs, (int)off, 0, 0));
+        const uint32_t off = (uint32_t)((s0 + s) * QS + lane % QS) * 8u;
+        vl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)off, 0, 0));
+        vd = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wrs, (int)off + 4, 0, 0));
     };
     auto store_step = [&](const u32x4 (&rg)[NL], float vl, float vd, int s, int st) {   // registers -> LDS
 #pragma unroll
@@ -307,7 +305,7 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         }
         if (tid < QS) {
             const int row = (s0 + s) * QS + tid;
-            s_lse[st][tid] = (row >= N || vl == -INFINITY) ? INFINITY : vl * kLog2e;   // +inf: no weight
+            s_lse[st][tid] = row >= N ? INFINITY : vl;   // +inf: no weight
         } else if (tid < 2 * QS) {
             s_D[st][tid - QS] = vd;
         }
@@ -473,8 +471,9 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     const auto vrs = make_rsrc(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
 
     // Q^T and dO^T B operands, and this row's D = sum_c dO_c O_c from the same
-    // column slices of O (summed over the four lane groups); D is also written
-    // for the dK/dV kernel, which runs after this one.
+    // column slices of O (summed over the four lane groups); D and the row's
+    // LSE log2 e are also written for the dK/dV kernel, which runs after this
+    // one.
     vec8 qop[KS], dop[KSV];
     float dpart = 0.f;
 #pragma unroll
@@ -496,7 +495,10 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     if (row < N) {
         const float L = lse[(int64_t)head * N + row];
         lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
-        if (g == 0) Dsum[(int64_t)head * N + row] = Drow;
+        if (g == 0) {
+            Dsum[((int64_t)head * N + row) * 2] = lse2;
+            Dsum[((int64_t)head * N + row) * 2 + 1] = Drow;
+        }
     }
 
     const int key_end = min(Nk, off_c + min(i0 + kWaves * 16, N));
@@ -668,7 +670,7 @@ hipError_t launch2(const BwdArgs &b) {
     const unsigned heads = (unsigned)(a.B * a.H);
     const float c = a.scale * kLog2e;
     const int off_c = a.causal ? (int)(a.Nk - a.N) : (int)a.Nk;
-    // dQ first: it also writes the row dots D that the dK/dV kernel reads.
+    // dQ first: it also writes the (LSE log2 e, D) pairs the dK/dV kernels read.
     const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
     hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV>), gq, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
@@ -677,6 +679,7 @@ hipError_t launch2(const BwdArgs &b) {
                        (int)a.Nk, off_c, c, a.scale, (int)heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (bwd_dkdv_mfma32_preferred(a.dtype, a.d, a.dv, a.N, a.causal)) return launch_bwd_dkdv_mfma32(b);
     const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, DV>), gk, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),

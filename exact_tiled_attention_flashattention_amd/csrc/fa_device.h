@@ -124,6 +124,20 @@ __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_
                  : "memory");
 }
 
+// The same copy with 4 bytes per lane (buffer_load_dword ... lds): lane i's
+// word lands at lds_addr + 4 i.
+__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dword %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
 // Stores a wave's 16 x W result tile (W = D or DV columns) as whole rows.
 // acc[db] holds the transposed 16x16 block db: lane (li, g) has columns
 // 16 db + 4g .. +3 of row li, which are multiplied by `mul` (per lane).  The lane's 8 bytes go to the wave's LDS slice

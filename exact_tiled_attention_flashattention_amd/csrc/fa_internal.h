@@ -40,7 +40,10 @@ struct BwdArgs {
     void *dq;             // [B, H, N, d]   (written)
     void *dk;             // [B, H, Nk, d]  (written)
     void *dv;             // [B, H, Nk, dv] (written)
-    float *Dsum;          // workspace [B, H, N]: D_i = sum_c dO_ic O_ic
+    float *Dsum;          // workspace [B, H, N, 2]: the matrix-core path keeps
+                          // (LSE_i log2 e, D_i) per row (+inf for a row that
+                          // sees no key), the VALU path D_i in the first B H N
+                          // floats; D_i = sum_c dO_ic O_ic
 };
 
 // Row-parallel VALU forward: any dtype, d and dv in {32, 64, 128, 256}.
@@ -81,5 +84,12 @@ int64_t decode_workgroups_per_split(int dtype, int64_t d, int64_t dv, int64_t B,
 hipError_t launch_bwd(const BwdArgs &b);
 bool bwd_mfma_supported(int dtype, int64_t d, int64_t dv);
 hipError_t launch_bwd_mfma(const BwdArgs &b);
+// dK/dV kernel on the 32x32x16 instruction (fa_bwd_mfma32.hip): bf16/fp16,
+// d = dv = 64; it reads the (LSE log2 e, D) pairs the dQ kernel of
+// fa_bwd_mfma.hip writes.  _preferred: the shapes where it is the faster
+// dK/dV kernel.
+bool bwd_dkdv_mfma32_supported(int dtype, int64_t d, int64_t dv);
+bool bwd_dkdv_mfma32_preferred(int dtype, int64_t d, int64_t dv, int64_t N, int causal);
+hipError_t launch_bwd_dkdv_mfma32(const BwdArgs &b);
 
 }  // namespace fa

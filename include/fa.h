@@ -221,8 +221,8 @@ int fa_decode_splitkv_auto_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                   int64_t d, int64_t dv, fa_dtype_t dtype);
 
 /*
- * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: one
- * float32 per query row, B * H * N * 4.  Returns 0 if an argument is < 1 or
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two
+ * float32 per query row, B * H * N * 8.  Returns 0 if an argument is < 1 or
  * the size overflows.
  */
 size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
@@ -244,7 +244,8 @@ size_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
  *   dq, dk, dv [B, H, N, d], [B, H, Nk, d], [B, H, Nk, dv], element type
  *              `dtype`, 16-byte aligned (written, round-to-nearest-even).
  *   workspace  device scratch of at least fa_bwd_workspace_size(B, H, N)
- *              bytes, 16-byte aligned, owned by the caller (the row dots D);
+ *              bytes, 16-byte aligned, owned by the caller (per query row
+ *              the row dot D and the LSE in base 2);
  *              contents on entry ignored, on exit undefined.
  * Arithmetic: products accumulated in float32; for bf16/fp16 the
  * probabilities and dS are rounded to `dtype` before the products that use

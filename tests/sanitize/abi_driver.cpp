@@ -146,7 +146,7 @@ void test_decode_noalloc() {
 
 void test_bwd() {
     const size_t ws = fa_bwd_workspace_size(4, 8, 300);
-    CHECK(ws == size_t(4) * 8 * 300 * 4);
+    CHECK(ws == size_t(4) * 8 * 300 * 8);
     CHECK(fa_bwd_workspace_size(std::numeric_limits<int64_t>::max(), 2, 2) == 0);
     const int before = stub::last.calls;
     CHECK(fa_bwd(P, P, P, P, L, nullptr, P, P, P, 4, 8, 300, 200, 64, 64, 1, 0.1f, FA_DTYPE_BF16,

@@ -162,7 +162,7 @@ def _bwd(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, B=1, H=1, N=4, Nk=
 
 
 def test_bwd_workspace_size():
-    assert fa.bwd_workspace_size(2, 3, 5) == 2 * 3 * 5 * 4
+    assert fa.bwd_workspace_size(2, 3, 5) == 2 * 3 * 5 * 8
     assert fa.bwd_workspace_size(0, 3, 5) == 0
     assert fa.bwd_workspace_size(1 << 40, 1 << 20, 1 << 20) == 0
 
@@ -187,7 +187,7 @@ def test_bwd_workspace_size():
     (dict(d=64, dvd=512), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(ws=A + 4), fa.FA_ERR_WORKSPACE),
-    (dict(B=2, H=3, N=5, wsb=2 * 3 * 5 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(B=2, H=3, N=5, wsb=2 * 3 * 5 * 8 - 1), fa.FA_ERR_WORKSPACE),
 ])
 def test_bwd_rejects(kw, expect):
     assert _bwd(**kw) == expect

@@ -39,6 +39,15 @@ def test_ragged(dtype, d, N, Nk, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N,Nk", [(2048, 2048), (2100, 2300), (2300, 2100)])
+def test_causal_long_rows_d64(dtype, N, Nk):
+    # d = 64 causal with N >= 2048 takes the 32-key-per-wave dK/dV kernel:
+    # several 256-key blocks and 64-row steps, ragged ends, N > Nk rows that
+    # see no key and N < Nk
+    _run(1, 2, N, Nk, 64, dtype, True, seed=N + Nk)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_several_blocks(dtype, d, causal):
