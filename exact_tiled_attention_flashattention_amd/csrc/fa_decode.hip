@@ -322,7 +322,7 @@ hipError_t launch_segment(const DecodeArgs &d) {
     return hipGetLastError();
 }
 
-// Segment kernel choice.  bf16/fp16 with d == dv <= 128 and at least
+// Segment kernel choice.  bf16/fp16 with d, dv <= 128 and at least
 // kMfmaMinRows rows per key/value head (grouped heads, several queries) run
 // on the matrix cores (fa_decode_mfma.hip): there the per-key work grows
 // with the rows and the VALU kernel below would stop being bound by memory.
@@ -331,7 +331,7 @@ hipError_t launch_segment(const DecodeArgs &d) {
 constexpr int64_t kMfmaMinRows = 2;
 
 bool use_mfma(int dtype, int64_t d, int64_t dv, int64_t rows) {
-    return dtype != kF32 && d == dv && d <= 128 && rows >= kMfmaMinRows;
+    return dtype != kF32 && d <= 128 && dv <= 128 && rows >= kMfmaMinRows;
 }
 int64_t valu_rows(int64_t rows) { return rows == 1 ? 1 : rows == 2 ? 2 : rows <= 4 ? 4 : 8; }
 

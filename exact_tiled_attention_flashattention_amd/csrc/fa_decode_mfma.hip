@@ -1,5 +1,5 @@
 // fa_decode_mfma.hip -- split-KV decode segment kernel on the matrix cores
-// (bf16/fp16 inputs, d == dv in {32, 64, 128}, fp32 accumulation).
+// (bf16/fp16 inputs, d and dv in {32, 64, 128}, fp32 accumulation).
 //
 // Method: CS349E Lecture 11 "flash_lab.py", section 4 (split_kv_decode):
 // each (segment, key/value head) is reduced to a normalised partial output
@@ -95,35 +95,42 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
     else return 0;
 }
 
-template <int VL>
-__device__ __forceinline__ void load_block(u32x4 (&kr)[VL], u32x4 (&vr)[VL],
+template <int VLK, int VLV>
+__device__ __forceinline__ void load_block(u32x4 (&kr)[VLK], u32x4 (&vr)[VLV],
                                            __amdgpu_buffer_rsrc_t krs,
-                                           __amdgpu_buffer_rsrc_t vrs, bool ok, uint32_t base,
-                                           const uint32_t (&gofs)[VL]) {
-    // `base` is the block's first byte; blocks past the wave's share read
-    // nothing (offsets outside the buffer return zeros without a memory access).
+                                           __amdgpu_buffer_rsrc_t vrs, bool ok, uint32_t kbase,
+                                           uint32_t vbase, const uint32_t (&gk)[VLK],
+                                           const uint32_t (&gv)[VLV]) {
+    // `kbase`, `vbase` are the block's first bytes in K and V; blocks past
+    // the wave's share read nothing (offsets outside the buffer return zeros
+    // without a memory access).
 #pragma unroll
-    for (int t = 0; t < VL; ++t) kr[t] = buffer_load16_nt(krs, ok ? base + gofs[t] : kOutOfRange);
+    for (int t = 0; t < VLK; ++t) kr[t] = buffer_load16_nt(krs, ok ? kbase + gk[t] : kOutOfRange);
 #pragma unroll
-    for (int t = 0; t < VL; ++t) vr[t] = buffer_load16_nt(vrs, ok ? base + gofs[t] : kOutOfRange);
+    for (int t = 0; t < VLV; ++t) vr[t] = buffer_load16_nt(vrs, ok ? vbase + gv[t] : kOutOfRange);
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int N, int Nk, int causal, float c,
     int num_splits, int seg_len, int G, int heads_kv, int tiles) {
     typedef typename Mma<T>::vec vec8;
     constexpr int KS = D / 32;              // contraction steps of S^T over d
-    constexpr int DB = D / 16;              // 16-column blocks of O^T
+    constexpr int DB = DV / 16;             // 16-column blocks of O^T
     constexpr int ROWB = 2 * D;             // bytes per key row
-    constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
-    constexpr int VL = kBlk * CPR / 64;     // 16-byte loads of K (and of V) per lane per block
-    constexpr int WBYTES = kBlk * ROWB;     // one K (or V) block; later the wave's O^T partials
-    static_assert(kRows == 16 && KS >= 1 && VL >= 1 && kRows * D * 4 == WBYTES, "shape");
+    constexpr int ROWBV = 2 * DV;           // bytes per value row
+    constexpr int CPR = ROWB / 16;          // 16-byte chunks per key row
+    constexpr int CPRV = ROWBV / 16;        // ... per value row
+    constexpr int VL = kBlk * CPR / 64;     // 16-byte loads of K per lane per block
+    constexpr int VLV = kBlk * CPRV / 64;   // ... of V
+    constexpr int WBYTES = kBlk * ROWB;     // one K block
+    constexpr int WBYTESV = kBlk * ROWBV;   // one V block; later the wave's O^T partials
+    static_assert(kRows == 16 && KS >= 1 && VL >= 1 && VLV >= 1 && kRows * DV * 4 == WBYTESV,
+                  "shape");
 
     __shared__ __attribute__((aligned(16))) unsigned char kbuf[kWaves][WBYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char vbuf[kWaves][WBYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char vbuf[kWaves][WBYTESV];
     __shared__ float sm_m[kWaves][kRows];
     __shared__ float sm_l[kWaves][kRows];
 
@@ -171,26 +178,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     };
     auto v_rsrc = [&](int kvh) {
         const int h = __builtin_amdgcn_readfirstlane(kvh);
-        return make_rsrc(v + (int64_t)h * Nk * D, (uint32_t)Nk * D * (uint32_t)sizeof(T));
+        return make_rsrc(v + (int64_t)h * Nk * DV, (uint32_t)Nk * DV * (uint32_t)sizeof(T));
     };
 
     // Per-lane byte offsets: global within a block (16-byte piece t * 64 +
     // lane of the block, row-major), LDS stores of K and V, and the LDS reads
     // of the K rows li, 16 + li (the swizzle is the same for both) and of V^T.
-    uint32_t gofs[VL], kw[VL], vw[VL], krd[KS], vrd[DB];
+    uint32_t gofs[VL], gofv[VLV], kw[VL], vw[VLV], krd[KS], vrd[DB];
 #pragma unroll
     for (int t = 0; t < VL; ++t) {
         const int slot = t * 64 + lane, row = slot / CPR, ch = slot % CPR;
         gofs[t] = ((uint32_t)row * D + ch * 8) * 2u;
         kw[t] = row * ROWB + ((ch ^ kswz<D>(row)) * 16);
-        vw[t] = row * ROWB + (((2 * ch) ^ vswz<D>(row)) * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < VLV; ++t) {
+        const int slot = t * 64 + lane, row = slot / CPRV, ch = slot % CPRV;
+        gofv[t] = ((uint32_t)row * DV + ch * 8) * 2u;
+        vw[t] = row * ROWBV + (((2 * ch) ^ vswz<DV>(row)) * 8);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) krd[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         const int r0 = 4 * g + li / 4;
-        vrd[db] = r0 * ROWB + (((4 * db + li % 4) ^ vswz<D>(r0)) * 8);
+        vrd[db] = r0 * ROWBV + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
     }
     unsigned char *kwb = kbuf[wave];
     unsigned char *wbuf = vbuf[wave];
@@ -207,17 +219,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     float m, l;
     f32x4 oacc[DB];
 
-    auto block_base = [&](int sb, int i) -> uint32_t {
-        return ((uint32_t)(sb + (wave + kWaves * i) * kBlk) * D) * 2u;
+    // First byte of the wave's i-th block in K (row width W = D) or V (DV).
+    auto block_base = [&](int sb, int i, int W) -> uint32_t {
+        return ((uint32_t)(sb + (wave + kWaves * i) * kBlk) * W) * 2u;
     };
 
     // One 32-key block of the current unit: scores, mask, online softmax,
     // O^T += V^T P^T.
-    auto step = [&](const u32x4 (&kr)[VL], const u32x4 (&vr)[VL], int i) {
+    auto step = [&](const u32x4 (&kr)[VL], const u32x4 (&vr)[VLV], int i) {
 #pragma unroll
         for (int t = 0; t < VL; ++t) *reinterpret_cast<u32x4 *>(kwb + kw[t]) = kr[t];
 #pragma unroll
-        for (int t = 0; t < VL; ++t) *reinterpret_cast<u32x4 *>(wbuf + vw[t]) = vr[t];
+        for (int t = 0; t < VLV; ++t) *reinterpret_cast<u32x4 *>(wbuf + vw[t]) = vr[t];
         f32x4 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
             oacc[db] *= alpha;
             const unsigned char *p = wbuf + vrd[db];
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWB));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWBV));
             const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             oacc[db] = Mma<T>::run(a, pb, oacc[db]);
         }
@@ -271,8 +284,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     // block's partner load fetches the next unit's first block and its Q is
     // loaded before the current unit's epilogue, so consecutive units stream
     // without a gap.
-    u32x4 kA[VL], vA[VL], kB[VL], vB[VL];
-    load_block<VL>(kA, vA, krs, vrs, 0 < mine, block_base(seg_begin, 0), gofs);
+    u32x4 kA[VL], vA[VLV], kB[VL], vB[VLV];
+    auto load = [&](u32x4 (&kr)[VL], u32x4 (&vr)[VLV], __amdgpu_buffer_rsrc_t ks,
+                    __amdgpu_buffer_rsrc_t vs, bool ok, int sb, int i) {
+        load_block<VL, VLV>(kr, vr, ks, vs, ok, block_base(sb, i, D), block_base(sb, i, DV), gofs, gofv);
+    };
+    load(kA, vA, krs, vrs, 0 < mine, seg_begin, 0);
     for (;;) {
         const int un = u + (int)gridDim.x;
         const bool has_next = un < units;
@@ -286,31 +303,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < mine; i += 2) {
-            load_block<VL>(kB, vB, krs, vrs, i + 1 < mine, block_base(seg_begin, i + 1), gofs);
+            load(kB, vB, krs, vrs, i + 1 < mine, seg_begin, i + 1);
             step(kA, vA, i);
             if (i + 2 < mine)
-                load_block<VL>(kA, vA, krs, vrs, true, block_base(seg_begin, i + 2), gofs);
+                load(kA, vA, krs, vrs, true, seg_begin, i + 2);
             else
-                load_block<VL>(kA, vA, nkrs, nvrs, nfirst, block_base(nbegin, 0), gofs);
+                load(kA, vA, nkrs, nvrs, nfirst, nbegin, 0);
             if (i + 1 < mine) step(kB, vB, i + 1);
         }
-        if (mine == 0) load_block<VL>(kA, vA, nkrs, nvrs, nfirst, block_base(nbegin, 0), gofs);
+        if (mine == 0) load(kA, vA, nkrs, nvrs, nfirst, nbegin, 0);
         vec8 qnext[KS];
         int nlimit = -1;
         if (has_next) load_q(nkvh, nrow0, qnext, nlimit);
 
         // ---- merge the 4 wave states of each row through LDS ----------------
         const float lt = rows4_sum(l);
-        float *ow = reinterpret_cast<float *>(wbuf);   // [16 rows][D], this wave's O^T
+        float *ow = reinterpret_cast<float *>(wbuf);   // [16 rows][DV], this wave's O^T
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(ow + li * D + 16 * db + 4 * g) = oacc[db];
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4 *>(ow + li * DV + 16 * db + 4 * g) = oacc[db];
         if (g == 0) {
             sm_m[wave][li] = m;
             sm_l[wave][li] = lt;
         }
         __syncthreads();
-        for (int idx = tid; idx < kRows * D; idx += kThreads) {
-            const int r = idx / D, col = idx % D;
+        for (int idx = tid; idx < kRows * DV; idx += kThreads) {
+            const int r = idx / DV, col = idx % DV;
             const int xr = row0 + r;
             if (xr >= G * N) continue;
             float mm = -INFINITY;
@@ -322,13 +339,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
                 for (int w = 0; w < kWaves; ++w) {
                     const float f = fast_exp2(sm_m[w][r] - mm);   // exp2(-inf) = 0
                     ll = fmaf(sm_l[w][r], f, ll);
-                    oo = fmaf(reinterpret_cast<const float *>(vbuf[w])[r * D + col], f, oo);
+                    oo = fmaf(reinterpret_cast<const float *>(vbuf[w])[r * DV + col], f, oo);
                 }
             }
-            // Workspace layout: o_s [B*Hq, S, N, D], lse_s [B*Hq, S, N].
+            // Workspace layout: o_s [B*Hq, S, N, DV], lse_s [B*Hq, S, N].
             const int64_t head = (int64_t)kvh * G + xr / N;
             const int64_t part = (head * num_splits + split) * N + xr % N;
-            ws_o[part * D + col] = ll > 0.f ? oo / ll : 0.f;
+            ws_o[part * DV + col] = ll > 0.f ? oo / ll : 0.f;
             if (col == 0) ws_lse[part] = ll > 0.f ? (mm + fast_log2(ll)) * kLn2 : -INFINITY;
         }
         __syncthreads();   // the partials in LDS are read before the next unit overwrites them
@@ -349,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
 }
 
 // Resident workgroups of one instantiation on the current device (cached).
-template <typename T, int D>
+template <typename T, int D, int DV>
 int resident_workgroups() {
     static int cache[64];
     int dev = 0;
@@ -360,7 +377,7 @@ int resident_workgroups() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&decode_segment_mfma_kernel<T, D>), kThreads,
+            &per_cu, reinterpret_cast<const void *>(&decode_segment_mfma_kernel<T, D, DV>), kThreads,
             0) != hipSuccess)
         return 0;
     val = cus * (per_cu > 0 ? per_cu : 1);
@@ -368,17 +385,17 @@ int resident_workgroups() {
     return val;
 }
 
-template <typename T, int D>
+template <typename T, int D, int DV>
 hipError_t launch_typed(const DecodeArgs &d) {
     const FwdArgs &a = d.a;
     const int G = (int)(a.H / d.Hkv);
     const int64_t tiles = ((int64_t)G * a.N + kRows - 1) / kRows;
     const int64_t units = (int64_t)d.num_splits * a.B * d.Hkv * tiles;
     if (units > 0x7fffffff) return hipErrorInvalidValue;
-    const int resident = resident_workgroups<T, D>();
+    const int resident = resident_workgroups<T, D, DV>();
     if (resident <= 0) return hipErrorInvalidDevice;
     const int64_t grid = units < resident ? units : resident;
-    hipLaunchKernelGGL((decode_segment_mfma_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads),
+    hipLaunchKernelGGL((decode_segment_mfma_kernel<T, D, DV>), dim3((unsigned)grid), dim3(kThreads),
                        0, a.stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), d.ws_o, d.ws_lse, (int)a.N, (int)a.Nk,
                        a.causal, a.scale * kLog2e, d.num_splits, (int)d.seg_len, G,
@@ -386,12 +403,22 @@ hipError_t launch_typed(const DecodeArgs &d) {
     return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_dv(const DecodeArgs &d) {
+    switch (d.a.dv) {
+        case 32: return launch_typed<T, D, 32>(d);
+        case 64: return launch_typed<T, D, 64>(d);
+        case 128: return launch_typed<T, D, 128>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T>
 hipError_t launch_dim(const DecodeArgs &d) {
     switch (d.a.d) {
-        case 32: return launch_typed<T, 32>(d);
-        case 64: return launch_typed<T, 64>(d);
-        case 128: return launch_typed<T, 128>(d);
+        case 32: return launch_dv<T, 32>(d);
+        case 64: return launch_dv<T, 64>(d);
+        case 128: return launch_dv<T, 128>(d);
         default: return hipErrorInvalidValue;
     }
 }

@@ -83,12 +83,13 @@ def test_decode_b8_h32_nk32768_d128_all_heads():
 # The definition: query head h attends with key/value head h // G, i.e.
 # standard attention on K and V with each key/value head repeated G times.
 
-def _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, num_splits, seed=0, std=1.0):
+def _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, num_splits, seed=0, std=1.0, dv=None):
     """`std` scales Q and K; V keeps unit scale (dividing by a power of two is
     exact), so the tolerance on O keeps its meaning."""
     Hq = Hkv * G
-    q, _, _ = make_inputs(B, Hq, N, 1, d, d, dtype, seed, std)
-    _, k, v = make_inputs(B, Hkv, 1, Nk, d, d, dtype, seed + 1000, std)
+    dv = d if dv is None else dv
+    q, _, _ = make_inputs(B, Hq, N, 1, d, dv, dtype, seed, std)
+    _, k, v = make_inputs(B, Hkv, 1, Nk, d, dv, dtype, seed + 1000, std)
     if std != 1.0:
         assert std == 2.0 ** round(math.log2(std))
         v = v / std
@@ -100,7 +101,8 @@ def _run_gqa(B, Hkv, G, N, Nk, d, dtype, causal, num_splits, seed=0, std=1.0):
     k_rep = k.repeat_interleave(G, dim=1).contiguous()
     v_rep = v.repeat_interleave(G, dim=1).contiguous()
     o_ref, l_ref = oracle_on(q, k_rep, v_rep, causal, scale)
-    compare(o, lse, o_ref, l_ref, dtype, f"gqa {dtype} {B}x{Hq}/{Hkv}x{N}x{Nk}x{d} S={num_splits}")
+    compare(o, lse, o_ref, l_ref, dtype,
+            f"gqa {dtype} {B}x{Hq}/{Hkv}x{N}x{Nk}x{d}/{dv} S={num_splits}")
     return q, k, v, o, lse
 
 
@@ -129,6 +131,18 @@ def test_gqa_many_rows_per_group(d):
 ])
 def test_gqa_matrix_core_shapes(dtype, d, G, N, Nk, splits, causal):
     _run_gqa(1, 2, G, N, Nk, d, dtype, causal, splits, seed=G + N + d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d,dv", [(32, 64), (32, 128), (64, 32), (64, 128), (128, 32), (128, 64)])
+@pytest.mark.parametrize("G,N,Nk,splits,causal", [
+    (16, 1, 95, 7, True),       # a full tile; ragged last block of 32 keys
+    (5, 4, 3, 2, True),         # N > Nk: row 0 of every head sees no key
+    (6, 3, 515, 5, False),      # 18 rows: two tiles, the second nearly empty
+])
+def test_gqa_matrix_core_unequal_dims(dtype, d, dv, G, N, Nk, splits, causal):
+    # K rows of d and V rows of dv elements on the matrix-core segment kernel
+    _run_gqa(1, 2, G, N, Nk, d, dtype, causal, splits, seed=G + N + d + dv, dv=dv)
 
 
 def test_gqa_large_scores():
