@@ -208,8 +208,10 @@ def test_bwd_rejects(kw, expect):
     ((12, 5, 1, 4, 1 << 20, 64, 64, torch.bfloat16), 32),    # 24 workgroups per split
     ((12, 5, 1, 4, 1 << 20, 64, 64, torch.float32), 16),     # 36 workgroups per split
     ((4, 8, 2, 1, 1 << 20, 128, 128, torch.float16), 64),     # 4 rows, one tile: 8 per split
-    # dv != d runs on the VALU kernel (8-row groups) even for bf16: 36 per split
-    ((12, 5, 1, 4, 1 << 20, 64, 128, torch.bfloat16), 16),
+    # dv != d (both <= 128) also runs on the matrix-core kernel: 24 per split
+    ((12, 5, 1, 4, 1 << 20, 64, 128, torch.bfloat16), 32),
+    # d = 256 runs on the VALU kernel (8-row groups) even for bf16: 36 per split
+    ((12, 5, 1, 4, 1 << 20, 256, 64, torch.bfloat16), 16),
 ])
 def test_auto_splits_rule(shape, expect):
     assert fa.decode_splitkv_auto_splits(*shape) == expect
