@@ -114,7 +114,10 @@ def cpu_baseline(q, k, v, s, causal, heads: int):
     """The FP64 oracle on the first ``heads`` heads of the prefill inputs."""
     import oracle
     import synth_inputs as si
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    # The oracle runs on at most 16 threads: a one-GPU box gives a job 16
+    # CPU threads, whatever the affinity mask shows.
+    available = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, available))
     qb = q.reshape(-1, s.N, s.d)[:heads]
     kb = k.reshape(-1, s.Nk, s.d)[:heads]
     vb = v.reshape(-1, s.Nk, s.dv)[:heads]
@@ -124,7 +127,8 @@ def cpu_baseline(q, k, v, s, causal, heads: int):
     orc.attention(qf, kf, vf, causal=causal, scale=1.0 / math.sqrt(s.d), nthreads=threads)
     dt = time.perf_counter() - t0
     flops = credited_flops(s, causal) * heads / (s.B * s.H)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "cores_in_affinity_mask": available, "kind": "oracle",
             "cpu": cpu_model(),
             "sample": f"{heads} of {s.B * s.H} heads of {PREFILL} (FP64 standard attention, "
                       f"{flops / 1e9:.1f} GFLOP credited, {dt:.2f} s wall on {threads} threads)"}
