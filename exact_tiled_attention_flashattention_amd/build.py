@@ -21,11 +21,11 @@ LIBRARY = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd_rowwise.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma_wide.hip", "fa_decode.hip",
            "fa_decode_mfma.hip", "fa_bwd.hip", "fa_bwd_mfma.hip",
            "fa_fwd_mfma_generic.hip", "fa_bwd_mfma32.hip"]
-# A second library, libfa_serial.so, differs only in fa_fwd_mfma_wide.hip,
-# built with FA_SERIAL_COPIES=1: every copy into LDS is waited for, between
+# A second library, libfa_serial.so, differs only in the SERIAL_SOURCES, built
+# with FA_SERIAL_COPIES=1: every copy into LDS is waited for, between
 # barriers, before it is read.  Its results must equal libfa.so's bit for
 # bit (a race check of the staging); only the tests load it.
-SERIAL_SOURCE = "fa_fwd_mfma_wide.hip"
+SERIAL_SOURCES = ["fa_fwd_mfma_wide.hip", "fa_bwd_mfma32.hip"]
 SERIAL_LIBRARY = os.path.join(PKG, "libfa_serial.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -54,11 +54,11 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     jobs = jobs or min(8, len(SOURCES))
     with cf.ThreadPoolExecutor(jobs) as ex:
         futs = [ex.submit(_compile, src) for src in SOURCES]
-        fut_serial = ex.submit(_compile, SERIAL_SOURCE, True)
+        futs_serial = {src.replace(".hip", ".o"): ex.submit(_compile, src, True)
+                       for src in SERIAL_SOURCES}
         objs = [f.result() for f in futs]
-        obj_serial = fut_serial.result()
-    serial_objs = [obj_serial if os.path.basename(o) == SERIAL_SOURCE.replace(".hip", ".o") else o
-                   for o in objs]
+        objs_serial = {name: f.result() for name, f in futs_serial.items()}
+    serial_objs = [objs_serial.get(os.path.basename(o), o) for o in objs]
     for lib, parts in ((LIBRARY, objs), (SERIAL_LIBRARY, serial_objs)):
         tmp = lib + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", tmp]

@@ -49,6 +49,16 @@ namespace {
 
 using namespace mfma32;
 
+// Checking build (FA_SERIAL_COPIES=1): each step's copies are issued between
+// two barriers and waited for before anyone reads them, so no copy is in
+// flight while LDS is read.  The arithmetic and its order are unchanged, so
+// this build's gradients must equal the pipelined build's bit for bit; only
+// the race-check tests load it.
+#ifndef FA_SERIAL_COPIES
+#define FA_SERIAL_COPIES 0
+#endif
+constexpr bool kSerialCopies = FA_SERIAL_COPIES != 0;
+
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKW = 32;                  // keys per wave
@@ -313,8 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // wave issues step s + 2's copies; before the barrier it waits until at
     // most step s + 1's copies are outstanding (copies complete in issue
     // order), so step s has landed for every wave once the barrier is passed.
-    if (nsteps > 0) issue(0, 0);
-    if (nsteps > 1) issue(1, 1);
+    if (nsteps > 0 && !kSerialCopies) issue(0, 0);
+    if (nsteps > 1 && !kSerialCopies) issue(1, 1);
     // The operand loads above complete before any copy (issue order), and
     // are waited for here so the loop carries no dependence on them.
     wait_vmcnt<0>();
@@ -326,9 +336,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // (unrolled by three so that each step's stage is a constant)
     auto step = [&](int s, auto STG) __attribute__((always_inline)) {
         constexpr int stage = decltype(STG)::value;
-        wait_pending(s + 1 < nsteps ? per_step : 0);
-        barrier();
-        if (s + 2 < nsteps) issue(s + 2, (stage + 2) % 3);
+        if (kSerialCopies) {
+            barrier();
+            issue(s, stage);
+            wait_pending(0);
+            barrier();
+        } else {
+            wait_pending(s + 1 < nsteps ? per_step : 0);
+            barrier();
+            if (s + 2 < nsteps) issue(s + 2, (stage + 2) % 3);
+        }
         compute(s, STG);
     };
     typedef std::integral_constant<int, 0> S0;

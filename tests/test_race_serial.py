@@ -1,9 +1,11 @@
-"""Race check of the wide matrix-core forward's LDS staging (GPU).
+"""Race checks of the LDS staging of the wide matrix-core forward and of the
+32-key dK/dV backward kernel (GPU).
 
-``libfa_serial.so`` is the same library with that kernel built with
-FA_SERIAL_COPIES=1: every K/V tile and Q block is copied between two
-barriers and waited for before it is read, so no copy is ever in flight
-while LDS is read and no stage is refilled early.  The arithmetic and
+``libfa_serial.so`` is the same library with those two kernels built with
+FA_SERIAL_COPIES=1: every K/V tile and Q block (backward: every Q/dO step
+and its (LSE, D) strip) is copied between two barriers and waited for
+before it is read, so no copy is ever in flight while LDS is read and no
+stage is refilled early.  The arithmetic and
 its order are the same, so both builds must give bit-identical O and LSE;
 a copy that landed late, or a stage overwritten while still being read, in
 the pipelined build (three stages, copies two tiles ahead and across items)
@@ -33,6 +35,9 @@ def _serial_lib():
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, c_int,
                            ctypes.c_float, c_int, vp]
     lib.fa_fwd.restype = c_int
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, c_int,
+                           ctypes.c_float, c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd.restype = c_int
     return lib
 
 
@@ -69,3 +74,33 @@ def test_pipelined_equals_serial_bitwise(dtype, B, H, N, Nk, d, dv, causal):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2), f"O differs: max {(o1.float() - o2.float()).abs().max().item()}"
     assert torch.equal(l1, l2) or torch.equal(torch.nan_to_num(l1), torch.nan_to_num(l2))
+
+
+BWD_CASES = [
+    (2, 3, 1000, 1000, False),      # d = 64 without the mask: several 256-key blocks, ragged
+    (1, 2, 2048, 2048, True),       # causal, 64-row steps across the diagonal
+    (1, 2, 2300, 2100, True),       # causal N > Nk: rows that see no key
+    (2, 2, 130, 700, False),        # one 64-row step, ragged keys
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H,N,Nk,causal", BWD_CASES)
+def test_backward_pipelined_equals_serial_bitwise(dtype, B, H, N, Nk, causal):
+    lib = _serial_lib()
+    q, k, v = make_inputs(B, H, N, Nk, 64, 64, dtype, seed=B + N + Nk)
+    dout, _, _ = make_inputs(B, H, N, 1, 64, 64, dtype, seed=N + 7)
+    scale = 0.125
+    log(f"bwd race check dtype={dtype} B={B} H={H} N={N} Nk={Nk} causal={causal}")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    g1 = fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=scale)
+    g2 = [torch.full_like(t, float("nan")) for t in (q, k, v)]
+    ws = torch.empty(fa.bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), g2[0].data_ptr(), g2[1].data_ptr(), g2[2].data_ptr(),
+                    B, H, N, Nk, 64, 64, int(causal), scale, 2 if dtype == "bf16" else 1,
+                    ws.data_ptr(), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, fa.status_string(st)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert torch.equal(a, b), f"{name} differs: max {(a.float() - b.float()).abs().max().item()}"
