@@ -277,26 +277,28 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
     int lim, full_end;
 
     // ---- S^T = K Q^T for the K tile in stage SK, into score buffer SP -----------
-    auto scores = [&](const int sk, auto SP) __attribute__((always_inline)) {
+    auto scores = [&](const int sk, auto SP, auto NKBC) __attribute__((always_inline)) {
         constexpr int P = decltype(SP)::value;
+        constexpr int NKB = decltype(NKBC)::value;   // 32-key blocks computed (2, or 1 on a half tile)
         const unsigned char *base = kbuf[0] + sk * TILE;
         sb[P][0] = f32x16{};
         sb[P][1] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < NKB; ++kb) {
                 const vec8 a = *reinterpret_cast<const vec8 *>(base + kb * 32 * ROWB + kofs[ks]);
                 sb[P][kb] = Mfma<T>::run(a, qop[ks], sb[P][kb]);
             }
         }
     };
     // ---- O^T += V^T P^T for the V tile in stage SV ---------------------------------
-    auto accumulate = [&](const int sv) __attribute__((always_inline)) {
+    auto accumulate = [&](const int sv, auto NKBC) __attribute__((always_inline)) {
+        constexpr int NKB = decltype(NKBC)::value;
         const unsigned char *base = vbuf[0] + sv * TILEV;
         typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 #pragma unroll
-        for (int cc = 0; cc < CC; ++cc) {
+        for (int cc = 0; cc < CC * NKB / 2; ++cc) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const unsigned char *p = base + cc * 16 * ROWBV + vofs[db];
@@ -308,13 +310,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
         }
     };
     // ---- masking of tile j (tiles that reach past the keys every row sees) ----
-    auto mask = [&](const int j, auto SP) __attribute__((always_inline)) {
+    auto mask = [&](const int j, auto SP, auto NKBC) __attribute__((always_inline)) {
         constexpr int P = decltype(SP)::value;
+        constexpr int NKB = decltype(NKBC)::value;
         const int j0 = j * kBC;
-        if (j0 + kBC > full_end) {
+        if (j0 + 32 * NKB > full_end) {
             const int t = lim - j0;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (32 * kb + 8 * (r / 4) + r % 4 > t) sb[P][kb][r] = -INFINITY;
@@ -327,11 +330,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
     // unchanged: O and l share the same m.  Returns the factor the output
     // accumulator must be multiplied by (1 unless m moved); the multiply is
     // left to the caller so that this code has no branch.
-    auto softmax = [&](auto SP) __attribute__((always_inline)) -> float {
+    auto softmax = [&](auto SP, auto NKBC) __attribute__((always_inline)) -> float {
         constexpr int P = decltype(SP)::value;
+        constexpr int NKB = decltype(NKBC)::value;
         float x = sb[P][0][0];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) x = __builtin_elementwise_maximum(x, sb[P][kb][r]);
         // The row's tile maximum exceeds m + 8 exactly when one of its two
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
         }
         const float m_use = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
-        for (int cc = 0; cc < CC; ++cc) {
+        for (int cc = 0; cc < CC * NKB / 2; ++cc) {
             f32x8 pf;
 #pragma unroll
             for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(fmaf(sb[P][cc / 2][8 * (cc % 2) + e], c, -m_use));
@@ -459,19 +463,28 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
             if (j == 0) prefetch_next();
         };
         // One computed tile: scores, mask, softmax, P V.
-        auto compute = [&](const int j, const int st) __attribute__((always_inline)) {
+        typedef std::integral_constant<int, 2> Full;
+        typedef std::integral_constant<int, 1> Half;
+        auto compute = [&](const int j, const int st, auto NKBC) __attribute__((always_inline)) {
             sync(j, st);
-            scores(st, I0{});
-            mask(j, I0{});
-            rescale(softmax(I0{}));
-            accumulate(st);
+            scores(st, I0{}, NKBC);
+            mask(j, I0{}, NKBC);
+            rescale(softmax(I0{}, NKBC));
+            accumulate(st, NKBC);
         };
         int j = 0, st = 0;
         auto step = [&]() __attribute__((always_inline)) {
             ++j;
             st = st == 2 ? 0 : st + 1;
         };
-        for (; j < wtiles; step()) compute(j, st);
+        // A last tile whose second 32-key block no row of the wave sees is
+        // computed as a half tile (its first block only).
+        const int jfull = (wtiles > 0 && (wtiles - 1) * kBC + 32 >= wave_end) ? wtiles - 1 : wtiles;
+        for (; j < jfull; step()) compute(j, st, Full{});
+        if (j < wtiles) {
+            compute(j, st, Half{});
+            step();
+        }
         // Tiles past this wave's rows: keep the workgroup's barriers and copies.
         for (; j < ntiles; step()) sync(j, st);
 
