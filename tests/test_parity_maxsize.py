@@ -90,3 +90,22 @@ def test_bwd_largest_head_slice():
     ref = oracle_bwd_on(q, k, v, dout, True, scale, heads=heads)
     got = tuple(torch.stack([g[b, h] for b, h in heads]) for g in (dq, dk, dv))
     compare_grads(got, ref, "bf16", f"bwd Nk={s.Nk}")
+
+
+def test_bwd_largest_head_slice_d64_unmasked():
+    # d = 64 without the mask runs the 32-key dK/dV kernel: one head of the
+    # largest accepted slice (the second, past 2 GiB) against the oracle.
+    from tests.parity import compare_grads, oracle_bwd_on
+    d = 64
+    s = si.Shape(1, 2, 8, _largest_nk(d), d, d)
+    log(f"fa_bwd largest head slice B=1 H=2 N=8 Nk={s.Nk} d={d} non-causal")
+    q, k, v = si.device_qkv(s, 27, "bf16", "cuda", 1.0)
+    dout, _, _ = si.device_qkv(si.Shape(1, 2, 8, 1, d, d), 28, "bf16", "cuda", 1.0)
+    scale = default_scale(d)
+    o, lse = fa.fwd(q, k, v, causal=False, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dout, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(0, 1)]
+    ref = oracle_bwd_on(q, k, v, dout, False, scale, heads=heads)
+    got = tuple(torch.stack([g[b, h] for b, h in heads]) for g in (dq, dk, dv))
+    compare_grads(got, ref, "bf16", f"bwd Nk={s.Nk} d={d}")
