@@ -33,6 +33,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import itertools
 import json
 import math
 import os
@@ -528,18 +529,22 @@ def bench_dims(args, torch, fa, si, dev) -> int:
                       "splits": S, "us": round(t * 1e6, 1), "gbs": round(nbytes / t / 1e9, 1),
                       "frac_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)})
         del q, k, v
-    # grouped-query decode, 4 query heads per key/value head
-    for d, dv in [(128, 128), (64, 64), (32, 32), (64, 128), (128, 64)]:
-        B, Hq, Hkv, Nk, S = 8, 32, 8, 32768, 64
+    # grouped-query decode, 4 query heads per key/value head, with 64 splits
+    # and with the automatic split count (num_splits = 0)
+    for (d, dv), S0 in itertools.product([(128, 128), (64, 64), (32, 32), (64, 128), (128, 64)],
+                                         (64, 0)):
+        B, Hq, Hkv, Nk = 8, 32, 8, 32768
+        S = S0 if S0 > 0 else fa.decode_splitkv_auto_splits(B, Hq, Hkv, 1, Nk, d, dv, torch.bfloat16)
         q, _, _ = si.device_qkv(si.Shape(B, Hq, 1, 1, d, dv), 15, "bf16", dev, 1.0)
         _, k, v = si.device_qkv(si.Shape(B, Hkv, 1, Nk, d, dv), 16, "bf16", dev, 1.0)
         ws = torch.empty(fa.decode_splitkv_workspace_size(B, Hq, 1, dv, S), dtype=torch.uint8,
                          device=dev)
-        t = _time_call(torch, lambda: fa.decode_splitkv_gqa(q, k, v, num_splits=S, workspace=ws),
+        t = _time_call(torch, lambda: fa.decode_splitkv_gqa(q, k, v, num_splits=S0, workspace=ws),
                        args.steps, args.warmup, stream)
         nbytes = B * Hkv * Nk * (d + dv) * 2 + B * Hq * ((d + dv) * 2 + 4)
         cases.append({"entry": "fa_decode_splitkv_gqa", "B": B, "Hq": Hq, "Hkv": Hkv, "Nk": Nk,
-                      "d": d, "dv": dv, "splits": S, "us": round(t * 1e6, 1),
+                      "d": d, "dv": dv, "splits": S if S0 > 0 else f"auto ({S})",
+                      "us": round(t * 1e6, 1),
                       "gbs": round(nbytes / t / 1e9, 1),
                       "frac_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)})
         del q, k, v
