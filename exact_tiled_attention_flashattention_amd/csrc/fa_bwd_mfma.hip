@@ -679,7 +679,7 @@ hipError_t launch2(const BwdArgs &b) {
                        (int)a.Nk, off_c, c, a.scale, (int)heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (bwd_dkdv_mfma32_preferred(a.dtype, a.d, a.dv, a.N, a.causal)) return launch_bwd_dkdv_mfma32(b);
+    if (bwd_dkdv_mfma32_preferred(b)) return launch_bwd_dkdv_mfma32(b);
     const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);
     hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<T, D, DV>), gk, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),

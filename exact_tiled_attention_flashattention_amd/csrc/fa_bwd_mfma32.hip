@@ -15,10 +15,11 @@
 // also writes, per query row, L2 = LSE log2(e) (+inf for a row that sees no
 // key) and D into the workspace, which this kernel reads.
 //
-// gfx950 mapping: a workgroup of 8 waves owns 256 keys of one head, 32 per
-// wave as the columns of 32x32 blocks; two waves per SIMD.  The wave's K and
-// V rows are B operands held in registers for the whole walk, and the walk
-// goes over the query rows in steps of 32:
+// gfx950 mapping: a workgroup of 8 waves owns a block of 256 keys of one
+// head at a time, 32 per wave as the columns of 32x32 blocks; two waves per
+// SIMD.  The wave's K and V rows are B operands held in registers for the
+// whole block, and the walk goes over the query rows in steps of 64 (two
+// 32-row sub-blocks):
 //  * S = Q K^T and dP = dO V^T: Q and dO are A operands read row-major from
 //    LDS; the 32x32 results give each lane one key (lane % 32) and 16 of the
 //    step's rows, 8 (r/4) + 4h + r%4 for register r (h = lane / 32);
@@ -31,8 +32,14 @@
 //  * each step's Q and dO are copied from memory straight into LDS twice,
 //    once XOR-swizzled for the row reads and once for the transposing reads
 //    (the forward kernel's conflict-free swizzles), together with the
-//    step's 32 (L2, D) pairs; three stages, each filled two steps ahead of
+//    step's 64 (L2, D) pairs; three stages, each filled two steps ahead of
 //    its use, one barrier per step.
+// Schedule: under the causal mask, with more blocks than the GPU holds
+// workgroups at once, the grid is persistent and a workgroup walks pairs of
+// blocks, k and nblk - 1 - k, whose steps add up to the same count for every
+// k; the copies of a block's first two steps are issued during the last two
+// steps of the block before, so only the operand loads of K and V are
+// exposed at a block's start.  Otherwise each block has a workgroup.
 // Under the causal mask (query i at position Nk - N + i) the walk starts at
 // the first row that sees the block's first key, a wave skips the steps in
 // which none of its keys is visible, and only steps that straddle the
@@ -65,27 +72,11 @@ constexpr int kKW = 32;                  // keys per wave
 constexpr int kBK = kWaves * kKW;        // keys per workgroup
 constexpr int kSB = 32;                  // query rows per sub-block (one 32x32 product)
 
-// This workgroup's (head, key block) in a 1-D grid of nblk * heads
-// workgroups.  Workgroup ids are dealt to the 8 XCDs round-robin; when heads
-// is a multiple of 8 the blocks of one head get ids congruent mod 8, so they
-// run on one XCD and share the head's Q and dO through its L2.
-__device__ __forceinline__ void work_item(int nblk, int heads, int &head, int &blk) {
-    const int L = blockIdx.x;
-    if (heads % 8 == 0) {
-        const int local = L / 8;
-        head = (local / nblk) * 8 + L % 8;
-        blk = local % nblk;
-    } else {
-        head = L / nblk;
-        blk = L % nblk;
-    }
-}
-
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_mfma32_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ ws, const T *__restrict__ dout, T *__restrict__ dk,
-    T *__restrict__ dvo, int N, int Nk, int off_c, float c, float scale, int heads) {
+    T *__restrict__ dvo, int N, int Nk, int off_c, float c, float scale, int heads, int paired) {
     typedef typename Mfma<T>::vec vec8;
     static_assert((D == 64 || D == 128) && (DV == 64 || DV == 128), "(d, dv)");
     constexpr int KS = D / 16;               // 16-wide contraction steps of S (over d)
@@ -116,34 +107,68 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     constexpr int NLD = 2 * QS / 64;                  // 4-byte wave copies of the (L2, D) strip
     __shared__ __attribute__((aligned(16))) unsigned char sbuf[LDS_BYTES];
 
-    int head, kblk;
-    work_item((Nk + kBK - 1) / kBK, heads, head, kblk);
-    const int j0 = kblk * kBK;
+    // LDS past the step stages: each wave's slice for its 32 output rows.
+    constexpr int OUTW = 2 * (D > DV ? D : DV) * kKW;  // bytes per wave slice
+    __shared__ __attribute__((aligned(16))) unsigned char obuf[kWaves * OUTW];
+
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int n = lane % 32;
     const int h = lane / 32;
-    const int kw0 = j0 + wave * kKW;
-    const int key = kw0 + n;                 // this lane's key (MFMA column)
 
-    // K^T and V^T B operands: lane holds row `key`, columns 16 ks + 8h .. +7.
-    vec8 kop[KS], vop[KSV];
-    {
-        const auto krs = make_rsrc(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
-        const auto vrs = make_rsrc(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kop[ks] = __builtin_bit_cast(vec8, buffer_load16(krs, ((uint32_t)key * D + ks * 16 + 8 * h) * 2u));
-#pragma unroll
-        for (int ks = 0; ks < KSV; ++ks)
-            vop[ks] = __builtin_bit_cast(vec8, buffer_load16(vrs, ((uint32_t)key * DV + ks * 16 + 8 * h) * 2u));
-    }
-
-    // Steps over query rows, from the first row that sees key j0.
-    const int first = max(0, j0 - off_c);
-    const int s0 = first / QS;
-    const int nsteps = max(0, (N + QS - 1) / QS - s0);
+    // ---- schedule ---------------------------------------------------------------
+    // Persistent: workgroup g walks units g, g + G, ...  When `paired`, a
+    // unit is a pair of key blocks of one head, k and nblk - 1 - k (the
+    // middle block alone when nblk is odd): under the causal mask their
+    // query steps add up to the same total for every k, so units cost the
+    // same.  Otherwise a unit is one key block.  When G and the head count
+    // are multiples of 8, units are numbered so that the workgroups of one
+    // XCD (ids congruent mod 8) work on the same heads at the same time and
+    // share their Q and dO through its L2.
+    const int nblk = (Nk + kBK - 1) / kBK;
+    const int U = paired ? (nblk + 1) / 2 : nblk;
+    const int n_units = heads * U;
+    const int G = gridDim.x;
+    const bool xcd_map = (G % 8 == 0) && (heads % 8 == 0);
+    const int qsteps = (N + QS - 1) / QS;
+    struct Item {
+        int t, half;              // unit round and which block of the pair
+        int head, j0, s0, nsteps; // head < 0: past the end
+    };
+    auto locate = [&](Item it) __attribute__((always_inline)) {
+        const int u = (int)blockIdx.x + it.t * G;
+        if (u >= n_units) {
+            it.head = -1;
+            it.nsteps = 0;
+            return it;
+        }
+        int pair;
+        if (xcd_map) {
+            const int local = u / 8;
+            it.head = (local / U) * 8 + u % 8;
+            pair = local % U;
+        } else {
+            it.head = u / U;
+            pair = u % U;
+        }
+        const int kblk = it.half == 0 ? pair : nblk - 1 - pair;
+        it.j0 = kblk * kBK;
+        // Steps over query rows, from the first row that sees key j0.
+        it.s0 = max(0, it.j0 - off_c) / QS;
+        it.nsteps = max(0, qsteps - it.s0);
+        return it;
+    };
+    auto next_item = [&](Item it) __attribute__((always_inline)) {
+        const int pair = it.half == 0 ? it.j0 / kBK : nblk - 1 - it.j0 / kBK;
+        if (paired && it.half == 0 && nblk - 1 - pair != pair) {
+            it.half = 1;
+        } else {
+            it.t += 1;
+            it.half = 0;
+        }
+        return locate(it);
+    };
 
     // Memory-to-LDS copies.  Copy i of a step (i = t kWaves + wave) writes
     // 1 KiB of the stage; lane l's 16 bytes land at offset 16 l of it, so the
@@ -206,33 +231,63 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 
     typedef __attribute__((address_space(3))) void lds_void;
     const uint32_t lds0 = (uint32_t)(size_t)(lds_void *)&sbuf[0];
-    const u32x4 qw = rsrc_words(q + (int64_t)head * N * D, (uint32_t)N * D * 2u);
-    const u32x4 ow = rsrc_words(dout + (int64_t)head * N * DV, (uint32_t)N * DV * 2u);
-    const u32x4 lw = rsrc_words(ws + (int64_t)head * N * 2, (uint32_t)N * 8u);
-    // Copies issued by this wave per step (every vector-memory operation of
-    // the loop is one of them).
+    // Copies issued by this wave per step.
     const int per_step = LPW + (wave < NLD ? 1 : 0);
-    auto issue = [&](int s, int stage) __attribute__((always_inline)) {
-        const uint32_t row0 = (uint32_t)((s0 + s) * QS);
+    // Steps are copied in the order they are consumed, across items, into
+    // stages 0, 1, 2, 0, ...: `con` counts the steps consumed, so a step's
+    // stage is its position in that stream mod 3.
+    // Every vector-memory operation before an item's first step has
+    // completed when it starts (the wait after its operand loads); inside
+    // the item the only ones are copies, which complete in issue order, so
+    // the wait before step s leaves outstanding what the step before issued
+    // (`prev` operations: the copies of step s + 1, or of the next item's
+    // first steps) and nothing else.
+    // (the counters travel as arguments and are written once per step, not
+    // in branches: captured by reference, or stored on some paths only,
+    // they would stay in memory)
+    struct Counts {
+        int con, prev, nissued;
+    } ps = {0, 0, 0};
+    // Buffer resources of one head's Q, dO and (L2, D) pairs.
+    struct Src {
+        u32x4 qw, ow, lw;
+    };
+    auto src_of = [=](int head_) __attribute__((always_inline)) {
+        Src w;
+        w.qw = rsrc_words(q + (int64_t)head_ * N * D, (uint32_t)N * D * 2u);
+        w.ow = rsrc_words(dout + (int64_t)head_ * N * DV, (uint32_t)N * DV * 2u);
+        w.lw = rsrc_words(ws + (int64_t)head_ * N * 2, (uint32_t)N * 8u);
+        return w;
+    };
+    auto issue = [=](const Src &w, int s0_, int s, int stage) __attribute__((always_inline)) {
+        const uint32_t row0 = (uint32_t)__builtin_amdgcn_readfirstlane((s0_ + s) * QS);
 #pragma unroll
         for (int t = 0; t < LPW; ++t)
-            lds_dma16(isq[t] ? qw : ow, __builtin_amdgcn_readfirstlane(lds0 + loff[t] + stage * tstride[t]),
+            lds_dma16(isq[t] ? u32x4(w.qw) : u32x4(w.ow), __builtin_amdgcn_readfirstlane(lds0 + loff[t] + stage * tstride[t]),
                       row0 * (isq[t] ? D : DV) * 2u + goff[t]);
         if (wave < NLD)
-            lds_dma4(lw, __builtin_amdgcn_readfirstlane(lds0 + OLD + stage * TL + wave * 256),
+            lds_dma4(w.lw, __builtin_amdgcn_readfirstlane(lds0 + OLD + stage * TL + wave * 256),
                      row0 * 8u + ldoff);
     };
+    auto consumed = [](Counts &c_) __attribute__((always_inline)) { ++c_.con; };
     auto barrier = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-
-    f32x16 dka[DBK], dva[DBV];
+    // K^T and V^T B operands of an item: lane holds row j0 + 32 wave + n,
+    // columns 16 ks + 8h .. +7.
+    auto load_kv = [&](int head_, int j0_, vec8 (&ko)[KS], vec8 (&vo)[KSV]) __attribute__((always_inline)) {
+        const int key = j0_ + wave * kKW + n;
+        const auto krs = make_rsrc(k + (int64_t)head_ * Nk * D, (uint32_t)Nk * D * 2u);
+        const auto vrs = make_rsrc(v + (int64_t)head_ * Nk * DV, (uint32_t)Nk * DV * 2u);
 #pragma unroll
-    for (int db = 0; db < DBK; ++db) dka[db] = f32x16{};
+        for (int ks = 0; ks < KS; ++ks)
+            ko[ks] = __builtin_bit_cast(vec8, buffer_load16(krs, ((uint32_t)key * D + ks * 16 + 8 * h) * 2u));
 #pragma unroll
-    for (int db = 0; db < DBV; ++db) dva[db] = f32x16{};
+        for (int ks = 0; ks < KSV; ++ks)
+            vo[ks] = __builtin_bit_cast(vec8, buffer_load16(vrs, ((uint32_t)key * DV + ks * 16 + 8 * h) * 2u));
+    };
 
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     auto tr_read = [&](const unsigned char *p, int rowb) __attribute__((always_inline)) {
@@ -241,10 +296,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
+    vec8 kop[KS], vop[KSV];
+    f32x16 dka[DBK], dva[DBV];
+    int kw0 = 0, key = 0;
+
     // Sub-block `sbk` (rows i0 .. i0 + 31, i0 = first row of the step + 32 sbk)
-    // of the step in stage `stage` (both compile-time constants here).
-    auto sub = [&](int i0, auto SBK, auto STG) __attribute__((always_inline)) {
-        constexpr int sbk = decltype(SBK)::value, stage = decltype(STG)::value;
+    // of the step in stage `stage`.
+    auto sub = [&](int i0, auto SBK, int stage) __attribute__((always_inline)) {
+        constexpr int sbk = decltype(SBK)::value;
         if (kw0 > off_c + i0 + kSB - 1) return;   // no row of the sub-block sees the wave's keys
         const unsigned char *sb = sbuf + stage * TQ + sbk * kSB * ROWQ;   // Q copies
         const unsigned char *so = sbuf + stage * TO + sbk * kSB * ROWO;   // dO copies
@@ -313,65 +372,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         }
     };
 
-    auto compute = [&](int s, auto STG) __attribute__((always_inline)) {
-        sub((s0 + s) * QS, std::integral_constant<int, 0>{}, STG);
-        if constexpr (NSB == 2) sub((s0 + s) * QS + kSB, std::integral_constant<int, 1>{}, STG);
+    auto compute = [&](int s0_, int s, int stage) __attribute__((always_inline)) {
+        sub((s0_ + s) * QS, std::integral_constant<int, 0>{}, stage);
+        if constexpr (NSB == 2) sub((s0_ + s) * QS + kSB, std::integral_constant<int, 1>{}, stage);
     };
 
-    // Step s lives in stage s % 3.  At step s, after the barrier (every
-    // wave is past step s - 1, whose stage is the one step s + 2 fills), the
-    // wave issues step s + 2's copies; before the barrier it waits until at
-    // most step s + 1's copies are outstanding (copies complete in issue
-    // order), so step s has landed for every wave once the barrier is passed.
-    if (nsteps > 0 && !kSerialCopies) issue(0, 0);
-    if (nsteps > 1 && !kSerialCopies) issue(1, 1);
-    // The operand loads above complete before any copy (issue order), and
-    // are waited for here so the loop carries no dependence on them.
-    wait_vmcnt<0>();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kop[ks]));
-#pragma unroll
-    for (int ks = 0; ks < KSV; ++ks) asm volatile("" : "+v"(vop[ks]));
-    // (unrolled by three so that each step's stage is a constant)
-    auto step = [&](int s, auto STG) __attribute__((always_inline)) {
-        constexpr int stage = decltype(STG)::value;
-        if (kSerialCopies) {
-            barrier();
-            issue(s, stage);
-            wait_pending(0);
-            barrier();
-        } else {
-            wait_pending(s + 1 < nsteps ? per_step : 0);
-            barrier();
-            if (s + 2 < nsteps) issue(s + 2, (stage + 2) % 3);
-        }
-        compute(s, STG);
-    };
-    typedef std::integral_constant<int, 0> S0;
-    typedef std::integral_constant<int, 1> S1;
-    typedef std::integral_constant<int, 2> S2;
-    int s = 0;
-    for (; s + 3 <= nsteps; s += 3) {
-        step(s, S0{});
-        step(s + 1, S1{});
-        step(s + 2, S2{});
-    }
-    if (s < nsteps) step(s, S0{});
-    if (s + 1 < nsteps) step(s + 1, S1{});
-
-    // ---- dK = scale (dK^T)^T and dV leave through LDS --------------------------
-    // Register r of block db holds column 32 db + 8 (r/4) + 4h + r%4 of key
-    // n.  Each wave writes its 32 rows (8-byte pieces, quads XOR-swizzled by
-    // the row so that one column's writes spread over the banks) into its
-    // own slice of the idle stages, reads them back 16 bytes per lane in row
-    // order and stores whole rows (bounds-checked: keys past Nk dropped).
-    __syncthreads();
-    auto store = [&](const auto &acc, auto WC, float mul, T *dst) __attribute__((always_inline)) {
+    // dK = scale (dK^T)^T and dV of an item leave through the wave's slice of
+    // obuf: register r of block db holds column 32 db + 8 (r/4) + 4h + r%4 of
+    // key n; the wave writes its 32 rows (8-byte pieces, quads XOR-swizzled
+    // by the row so that one column's writes spread over the banks), reads
+    // them back 16 bytes per lane in row order and stores whole rows
+    // (bounds-checked: keys past Nk dropped).  Only this wave uses its slice.
+    auto store = [&](int head_, const auto &acc, auto WC, float mul, T *dst) __attribute__((always_inline)) {
         constexpr int W = decltype(WC)::value;
         constexpr int NB = W / 32, ROWB = 2 * W, CPR = ROWB / 16;
         typedef T t4 __attribute__((ext_vector_type(4)));
-        unsigned char *buf = sbuf + wave * kKW * ROWB;
+        unsigned char *buf = obuf + wave * OUTW;
 #pragma unroll
         for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -382,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
                 const int u = (8 * db + 2 * a + h) ^ (2 * (n & 7));
                 *reinterpret_cast<t4 *>(buf + n * ROWB + u * 8) = x;
             }
-        const auto rs = make_rsrc(dst + (int64_t)head * Nk * W, (uint32_t)Nk * W * 2u);
+        const auto rs = make_rsrc(dst + (int64_t)head_ * Nk * W, (uint32_t)Nk * W * 2u);
 #pragma unroll
         for (int t = 0; t < kKW * CPR / 64; ++t) {
             const int ch = t * 64 + lane;
@@ -391,9 +407,126 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
             __builtin_amdgcn_raw_buffer_store_b128(x, rs, (int)((uint32_t)(kw0 + r) * ROWB + pc * 16), 0, 2);
         }
     };
-    static_assert(kWaves * kKW * 2 * (D > DV ? D : DV) <= LDS_BYTES, "output staging fits");
-    store(dka, std::integral_constant<int, D>{}, scale, dk);
-    store(dva, std::integral_constant<int, DV>{}, 1.f, dvo);
+
+    // ---- the walk ---------------------------------------------------------------
+    // At step s of an item, after the barrier (every wave is past the step
+    // before, whose stage is the one two steps ahead fills), the wave issues
+    // the copies of the step two ahead in the stream, which is the next
+    // item's step 0 or 1 near an item's end; before the barrier it waits
+    // until only the copies issued after this step's are outstanding.  The
+    // next item's first two steps that were not fetched ahead, and its
+    // operands, are fetched when it starts, and waited for there.
+    auto wait_prev = [&](int prev) __attribute__((always_inline)) {
+        if (prev == 0) wait_vmcnt<0>();
+        else if (wave < NLD) wait_vmcnt<LPW + 1>();
+        else wait_vmcnt<LPW>();
+    };
+    auto start = [&](const Item &it) __attribute__((always_inline)) {
+        load_kv(it.head, it.j0, kop, vop);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kop[ks]));
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) asm volatile("" : "+v"(vop[ks]));
+    };
+    Item cur;
+    cur.t = 0;
+    cur.half = 0;
+    cur = locate(cur);
+    if (cur.head < 0) return;
+    {
+        const Src w = src_of(cur.head);
+        if (!kSerialCopies)
+            for (int s = 0; s < 2 && s < cur.nsteps; ++s) issue(w, cur.s0, s, s);
+        start(cur);
+    }
+    for (;;) {
+        const Item nxt = next_item(cur);
+        const Src cw = src_of(cur.head);
+        ps.prev = 0;
+        ps.nissued = 0;   // steps of nxt already fetched
+        kw0 = cur.j0 + wave * kKW;
+        key = kw0 + n;
+#pragma unroll
+        for (int db = 0; db < DBK; ++db) dka[db] = f32x16{};
+#pragma unroll
+        for (int db = 0; db < DBV; ++db) dva[db] = f32x16{};
+        // One step in stage ST (a compile-time constant, so that every LDS
+        // address of the step is an immediate offset); the stage cycles
+        // 0, 1, 2 in the order of the stream.
+        auto step = [&](Counts &ps_, const Item cur_, const Item nxt_, int s, auto ST) __attribute__((always_inline)) {
+            constexpr int st = decltype(ST)::value;
+            if (kSerialCopies) {
+                barrier();
+                issue(cw, cur_.s0, s, st);
+                wait_vmcnt<0>();
+                barrier();
+            } else {
+                wait_prev(ps_.prev);
+                barrier();
+                const int jn = s + 2 - cur_.nsteps;   // >= 0: the next item's step
+                const bool ahead_next = jn >= 0 && nxt_.head >= 0 && jn == ps_.nissued && jn < nxt_.nsteps;
+                if (jn < 0) {
+                    issue(cw, cur_.s0, s + 2, (st + 2) % 3);
+                } else if (ahead_next) {
+                    // (an opaque copy keeps the compiler from holding the
+                    // next head's resources across the whole loop)
+                    int hd = nxt_.head;
+                    asm volatile("" : "+s"(hd));
+                    issue(src_of(hd), nxt_.s0, jn, (st + 2) % 3);
+                }
+                ps_.nissued += ahead_next ? 1 : 0;
+                ps_.prev = jn < 0 || ahead_next ? per_step : 0;
+            }
+            compute(cur_.s0, s, st);
+            consumed(ps_);
+        };
+        typedef std::integral_constant<int, 0> S0;
+        typedef std::integral_constant<int, 1> S1;
+        typedef std::integral_constant<int, 2> S2;
+        // The item's first steps up to the next stage 0, then steps in
+        // threes (stages 0, 1, 2), then the last one or two.
+        const int n_ = cur.nsteps, ph = ps.con % 3;
+        int s = 0;
+        if (ph == 1 && s < n_) step(ps, cur, nxt, s++, S1{});
+        if (ph >= 1 && s < n_) step(ps, cur, nxt, s++, S2{});
+        for (; s + 3 <= n_; s += 3) {
+            step(ps, cur, nxt, s, S0{});
+            step(ps, cur, nxt, s + 1, S1{});
+            step(ps, cur, nxt, s + 2, S2{});
+        }
+        if (s < n_) step(ps, cur, nxt, s, S0{});
+        if (s + 1 < n_) step(ps, cur, nxt, s + 1, S1{});
+        store(cur.head, dka, std::integral_constant<int, D>{}, scale, dk);
+        store(cur.head, dva, std::integral_constant<int, DV>{}, 1.f, dvo);
+        if (nxt.head < 0) break;
+        const Src nw = src_of(nxt.head);
+        if (!kSerialCopies)
+            for (int s = ps.nissued; s < 2 && s < nxt.nsteps; ++s) issue(nw, nxt.s0, s, (ps.con + s) % 3);
+        start(nxt);
+        cur = nxt;
+    }
+}
+
+// Resident workgroups of one instantiation on the current device (cached).
+template <typename T, int D, int DV>
+int resident_workgroups() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int val = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (val > 0) return val;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&bwd_dkdv_mfma32_kernel<T, D, DV>), kThreads,
+            0) != hipSuccess)
+        return 0;
+    val = cus * (per_cu > 0 ? per_cu : 1);
+    __atomic_store_n(&cache[dev], val, __ATOMIC_RELAXED);
+    return val;
 }
 
 template <typename T, int D, int DV>
@@ -401,12 +534,21 @@ hipError_t launch(const BwdArgs &b) {
     const FwdArgs &a = b.a;
     const unsigned heads = (unsigned)(a.B * a.H);
     const int off_c = a.causal ? (int)(a.Nk - a.N) : (int)a.Nk;
-    const dim3 grid((unsigned)((a.Nk + kBK - 1) / kBK) * heads);
+    const int64_t nblk = (a.Nk + kBK - 1) / kBK;
+    const int resident = resident_workgroups<T, D, DV>();
+    if (resident <= 0) return hipErrorInvalidDevice;
+    // Under the causal mask: pairs of blocks, where there are more blocks
+    // than resident workgroups, and a persistent grid.  Without it every
+    // block costs the same, and one workgroup per block measured faster
+    // than walking them.
+    const int paired = a.causal && (int64_t)heads * nblk > resident ? 1 : 0;
+    const int64_t units = (int64_t)heads * (paired ? (nblk + 1) / 2 : nblk);
+    const dim3 grid((unsigned)(a.causal && units > resident ? resident : units));
     hipLaunchKernelGGL((bwd_dkdv_mfma32_kernel<T, D, DV>), grid, dim3(kThreads), 0, a.stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), b.Dsum, static_cast<const T *>(b.dout),
                        static_cast<T *>(b.dk), static_cast<T *>(b.dv), (int)a.N, (int)a.Nk, off_c,
-                       a.scale * kLog2e, a.scale, (int)heads);
+                       a.scale * kLog2e, a.scale, (int)heads, paired);
     return hipGetLastError();
 }
 
@@ -423,13 +565,16 @@ bool bwd_dkdv_mfma32_supported(int dtype, int64_t d, int64_t dv) {
     return (dtype == kBF16 || dtype == kF16) && d == 64 && dv == 64;
 }
 
-// Measured against the 16-key kernel of fa_bwd_mfma.hip (B x H x N, d = 64,
-// paired HIP-event timings): 7-10% faster without the mask and on causal
-// rows of 4096 or more, level at causal 2048, 4% slower at causal 1024,
-// where its 256-key blocks leave more of each workgroup on the diagonal and
-// the single resident workgroup per CU exposes each block's start.
-bool bwd_dkdv_mfma32_preferred(int dtype, int64_t d, int64_t dv, int64_t N, int causal) {
-    return bwd_dkdv_mfma32_supported(dtype, d, dv) && (!causal || N >= 2048);
+// Under the causal mask with fewer 256-key blocks than resident workgroups
+// the 16-key kernel of fa_bwd_mfma.hip, whose blocks are half as long, keeps
+// more of the GPU busy (B1 x H16 x 1024: 47 us against 54 us).
+bool bwd_dkdv_mfma32_preferred(const BwdArgs &b) {
+    const FwdArgs &a = b.a;
+    if (!bwd_dkdv_mfma32_supported(a.dtype, a.d, a.dv)) return false;
+    if (!a.causal) return true;
+    const int resident = a.dtype == kBF16 ? resident_workgroups<bf16_t, 64, 64>()
+                                          : resident_workgroups<f16_t, 64, 64>();
+    return a.B * a.H * ((a.Nk + kBK - 1) / kBK) >= resident;
 }
 
 hipError_t launch_bwd_dkdv_mfma32(const BwdArgs &b) {

@@ -89,7 +89,7 @@ hipError_t launch_bwd_mfma(const BwdArgs &b);
 // fa_bwd_mfma.hip writes.  _preferred: the shapes where it is the faster
 // dK/dV kernel.
 bool bwd_dkdv_mfma32_supported(int dtype, int64_t d, int64_t dv);
-bool bwd_dkdv_mfma32_preferred(int dtype, int64_t d, int64_t dv, int64_t N, int causal);
+bool bwd_dkdv_mfma32_preferred(const BwdArgs &b);
 hipError_t launch_bwd_dkdv_mfma32(const BwdArgs &b);
 
 }  // namespace fa

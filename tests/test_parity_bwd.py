@@ -90,3 +90,21 @@ def test_prefill_b64_h16_n1024_d64_all_heads():
         ref = oracle_bwd_on(q[sl], k[sl], v[sl], dout[sl], True, scale)
         compare_grads((dq[sl], dk[sl], dv[sl]), ref, "bf16", f"bwd full-size batches {b0}..{b0 + 7}")
     log(f"  bwd full-size: {s.B * s.H}/{s.B * s.H} heads compared element by element")
+
+
+@pytest.mark.parametrize("B,H,N,Nk,causal", [(8, 16, 1024, 1024, False), (5, 7, 1800, 1900, True)])
+def test_several_blocks_per_workgroup_all_heads(B, H, N, Nk, causal):
+    """Shapes with more 256-key blocks than the GPU holds workgroups at once:
+    under the mask one workgroup of the d = 64 dK/dV kernel walks several
+    pairs of blocks (here with a head count that is not a multiple of 8),
+    without it each block has a workgroup of its own.  Every element of the
+    gradients of every head against the oracle."""
+    q, k, v, dout = _inputs(B, H, N, Nk, 64, "bf16", seed=N + Nk)
+    scale = default_scale(64)
+    log(f"fa_bwd several blocks per workgroup B={B} H={H} N={N} Nk={Nk} causal={causal}")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle_bwd_on(q, k, v, dout, causal, scale)
+    compare_grads((dq, dk, dv), ref, "bf16", f"bwd B={B} H={H} N={N} Nk={Nk}")

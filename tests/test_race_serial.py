@@ -81,6 +81,12 @@ BWD_CASES = [
     (1, 2, 2048, 2048, True),       # causal, 64-row steps across the diagonal
     (1, 2, 2300, 2100, True),       # causal N > Nk: rows that see no key
     (2, 2, 130, 700, False),        # one 64-row step, ragged keys
+    # causal with more 256-key blocks than resident workgroups: each
+    # workgroup walks pairs of blocks and copies the next block's first steps
+    # during the last steps of the one before
+    (8, 16, 2048, 2048, True),      # two pairs per workgroup
+    (5, 7, 1800, 1900, True),       # head count not a multiple of 8, ragged
+    (8, 16, 1024, 1024, False),     # unmasked: 512 blocks, one per workgroup
 ]
 
 
