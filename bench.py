@@ -273,8 +273,8 @@ def summarize_trace(directory: str) -> None:
         f"decode_splitkv_gqa_{GQA_WORKLOAD}.txt": ("decode_segment_mfma_kernel",
                                                    ("decode_segment_mfma_kernel",
                                                     "decode_merge_kernel"), gqa_cmd),
-        f"bwd_mfma_{PREFILL}.txt": ("bwd_dkdv_mfma_kernel",
-                                    ("bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel",
+        f"bwd_mfma_{PREFILL}.txt": ("bwd_dq_mfma_kernel",
+                                    ("bwd_dkdv_mfma", "bwd_dq_mfma_kernel",
                                      "bwd_dot_kernel"), bwd_cmd),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -473,7 +473,7 @@ def bench_bwd(args, torch, fa, si, dev) -> int:
         "data": "synthetic (seeded torch Philox draws on the GPU)",
         "config": {"workload": PREFILL + " (fa_bwd)", "B": s.B, "H": s.H, "N": s.N, "Nk": s.Nk,
                    "d": s.d, "causal": True},
-        "roofline": {"kernel": "bwd_dq_mfma_kernel + bwd_dkdv_mfma_kernel",
+        "roofline": {"kernel": "bwd_dq_mfma_kernel + bwd_dkdv_mfma32_kernel",
                      "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "avg_launch_us": round(avg_s * 1e6, 2), "min_launch_us": round(min(ms) * 1e3, 2),
@@ -531,7 +531,8 @@ def bench_dims(args, torch, fa, si, dev) -> int:
         del q, k, v
     # grouped-query decode, 4 query heads per key/value head, with 64 splits
     # and with the automatic split count (num_splits = 0)
-    for (d, dv), S0 in itertools.product([(128, 128), (64, 64), (32, 32), (64, 128), (128, 64)],
+    for (d, dv), S0 in itertools.product([(128, 128), (64, 64), (32, 32), (64, 128), (128, 64),
+                                          (256, 256)],
                                          (64, 0)):
         B, Hq, Hkv, Nk = 8, 32, 8, 32768
         S = S0 if S0 > 0 else fa.decode_splitkv_auto_splits(B, Hq, Hkv, 1, Nk, d, dv, torch.bfloat16)

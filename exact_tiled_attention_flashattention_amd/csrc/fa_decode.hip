@@ -322,16 +322,18 @@ hipError_t launch_segment(const DecodeArgs &d) {
     return hipGetLastError();
 }
 
-// Segment kernel choice.  bf16/fp16 with d, dv <= 128 and at least
-// kMfmaMinRows rows per key/value head (grouped heads, several queries) run
-// on the matrix cores (fa_decode_mfma.hip): there the per-key work grows
-// with the rows and the VALU kernel below would stop being bound by memory.
+// Segment kernel choice.  bf16/fp16 with d, dv <= 128 or d = dv = 256, and
+// at least kMfmaMinRows rows per key/value head (grouped heads, several
+// queries) run on the matrix cores (fa_decode_mfma.hip): there the per-key
+// work grows with the rows and the VALU kernel below would stop being bound
+// by memory.
 // Otherwise the VALU kernel runs with the smallest of 1, 2, 4, 8 rows per
 // workgroup that covers the rows (8 at most; more rows take more workgroups).
 constexpr int64_t kMfmaMinRows = 2;
 
 bool use_mfma(int dtype, int64_t d, int64_t dv, int64_t rows) {
-    return dtype != kF32 && d <= 128 && dv <= 128 && rows >= kMfmaMinRows;
+    return dtype != kF32 && ((d <= 128 && dv <= 128) || (d == 256 && dv == 256)) &&
+           rows >= kMfmaMinRows;
 }
 int64_t valu_rows(int64_t rows) { return rows == 1 ? 1 : rows == 2 ? 2 : rows <= 4 ? 4 : 8; }
 

@@ -1,5 +1,6 @@
 // fa_decode_mfma.hip -- split-KV decode segment kernel on the matrix cores
-// (bf16/fp16 inputs, d and dv in {32, 64, 128}, fp32 accumulation).
+// (bf16/fp16 inputs, d and dv in {32, 64, 128}, and d = dv = 256; fp32
+// accumulation).
 //
 // Method: CS349E Lecture 11 "flash_lab.py", section 4 (split_kv_decode):
 // each (segment, key/value head) is reduced to a normalised partial output
@@ -31,6 +32,12 @@
 //    LDS with the same rule and written to the workspace as (o_s, lse_s).
 //    The next unit's first block and Q rows are already being fetched then,
 //    so a workgroup streams from one unit into the next without a gap.
+//  * d = dv = 256: a block is 32 KiB of K and V per wave, so one register
+//    set holds the block in flight (the next block's loads are issued right
+//    after the current block has moved to LDS), and one workgroup of 4
+//    waves per CU has the 128 KiB of LDS and one wave per SIMD the
+//    registers; the 4 waves' independent streams keep 128 KiB per CU in
+//    flight.
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -84,13 +91,13 @@ __device__ __forceinline__ float rows4_sum(float x) {
 // multiple of 4, so 16-byte chunks stay whole), for the transposing reads
 // of rows 4g + i/4, quads 4 db + i%4.
 template <int D> __device__ __forceinline__ int kswz(int r) {
-    if constexpr (D == 128) return r & 15;
+    if constexpr (D >= 128) return r & 15;
     else if constexpr (D == 64)
         return ((r >> 2) & 1) | ((__builtin_popcount(r & 15) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
     else return r & 3;
 }
 template <int D> __device__ __forceinline__ int vswz(int r) {
-    if constexpr (D == 128) return 4 * (r & 7);
+    if constexpr (D >= 128) return 4 * (r & 7);
     else if constexpr (D == 64) return 4 * ((r & 3) ^ ((r >> 2) & 1));
     else return 0;
 }
@@ -99,19 +106,25 @@ template <int VLK, int VLV>
 __device__ __forceinline__ void load_block(u32x4 (&kr)[VLK], u32x4 (&vr)[VLV],
                                            __amdgpu_buffer_rsrc_t krs,
                                            __amdgpu_buffer_rsrc_t vrs, bool ok, uint32_t kbase,
-                                           uint32_t vbase, const uint32_t (&gk)[VLK],
-                                           const uint32_t (&gv)[VLV]) {
-    // `kbase`, `vbase` are the block's first bytes in K and V; blocks past
-    // the wave's share read nothing (offsets outside the buffer return zeros
-    // without a memory access).
+                                           uint32_t vbase, uint32_t lane16) {
+    // `kbase`, `vbase` are the block's first bytes in K and V; piece t of a
+    // block is its bytes 1024 t + 16 lane .. +15 (whole consecutive rows).
+    // Blocks past the wave's share read nothing (offsets outside the buffer
+    // return zeros without a memory access).
 #pragma unroll
-    for (int t = 0; t < VLK; ++t) kr[t] = buffer_load16_nt(krs, ok ? kbase + gk[t] : kOutOfRange);
+    for (int t = 0; t < VLK; ++t)
+        kr[t] = buffer_load16_nt(krs, ok ? kbase + 1024u * t + lane16 : kOutOfRange);
 #pragma unroll
-    for (int t = 0; t < VLV; ++t) vr[t] = buffer_load16_nt(vrs, ok ? vbase + gv[t] : kOutOfRange);
+    for (int t = 0; t < VLV; ++t)
+        vr[t] = buffer_load16_nt(vrs, ok ? vbase + 1024u * t + lane16 : kOutOfRange);
 }
 
+// One register set for the block in flight where a block is too large for
+// two (d = dv = 256), and then one workgroup per CU.
+template <int D, int DV> constexpr bool single_set() { return D + DV > 256; }
+
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
+__global__ __launch_bounds__(kThreads, (single_set<D, DV>() ? 1 : 2)) void decode_segment_mfma_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     float *__restrict__ ws_o, float *__restrict__ ws_lse, int N, int Nk, int causal, float c,
     int num_splits, int seg_len, int G, int heads_kv, int tiles) {
@@ -181,29 +194,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
         return make_rsrc(v + (int64_t)h * Nk * DV, (uint32_t)Nk * DV * (uint32_t)sizeof(T));
     };
 
-    // Per-lane byte offsets: global within a block (16-byte piece t * 64 +
-    // lane of the block, row-major), LDS stores of K and V, and the LDS reads
-    // of the K rows li, 16 + li (the swizzle is the same for both) and of V^T.
-    uint32_t gofs[VL], gofv[VLV], kw[VL], vw[VLV], krd[KS], vrd[DB];
+    // Per-lane byte offsets: LDS stores of K and V (16-byte piece t * 64 +
+    // lane of the block, row-major), and the LDS reads of the K rows li,
+    // 16 + li (the swizzle is the same for both) and of V^T.  The swizzles
+    // repeat every 16 rows (K) and 8 rows (V), and touch only the low 16
+    // chunks (K) and 32 quads (V) of a row, so only one period of each is
+    // held in registers and the rest is an immediate offset from it.
+    constexpr int RPT = 64 / CPR, RPTV = 64 / CPRV;            // rows per piece index
+    constexpr int PK = RPT >= 16 ? 1 : 16 / RPT, PV = RPTV >= 8 ? 1 : 8 / RPTV;
+    constexpr int PKS = KS < 4 ? KS : 4, PDB = DB < 8 ? DB : 8;
+    static_assert(VL % PK == 0 && VLV % PV == 0, "swizzle periods");
+    uint32_t kwp[PK], vwp[PV], krdp[PKS], vrdp[PDB];
 #pragma unroll
-    for (int t = 0; t < VL; ++t) {
+    for (int t = 0; t < PK; ++t) {
         const int slot = t * 64 + lane, row = slot / CPR, ch = slot % CPR;
-        gofs[t] = ((uint32_t)row * D + ch * 8) * 2u;
-        kw[t] = row * ROWB + ((ch ^ kswz<D>(row)) * 16);
+        kwp[t] = row * ROWB + ((ch ^ kswz<D>(row)) * 16);
     }
 #pragma unroll
-    for (int t = 0; t < VLV; ++t) {
+    for (int t = 0; t < PV; ++t) {
         const int slot = t * 64 + lane, row = slot / CPRV, ch = slot % CPRV;
-        gofv[t] = ((uint32_t)row * DV + ch * 8) * 2u;
-        vw[t] = row * ROWBV + (((2 * ch) ^ vswz<DV>(row)) * 8);
+        vwp[t] = row * ROWBV + (((2 * ch) ^ vswz<DV>(row)) * 8);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) krd[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
+    for (int ks = 0; ks < PKS; ++ks) krdp[ks] = li * ROWB + (((ks * 4 + g) ^ kswz<D>(li)) * 16);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < PDB; ++db) {
         const int r0 = 4 * g + li / 4;
-        vrd[db] = r0 * ROWBV + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
+        vrdp[db] = r0 * ROWBV + (((4 * db + li % 4) ^ vswz<DV>(r0)) * 8);
     }
+    auto kw = [&](int t) { return kwp[t % PK] + (t / PK) * (PK * RPT) * ROWB; };
+    auto vw = [&](int t) { return vwp[t % PV] + (t / PV) * (PV * RPTV) * ROWBV; };
+    auto krd = [&](int ks) { return krdp[ks % 4 % PKS] + (ks / 4) * 256; };
+    auto vrd = [&](int db) { return vrdp[db % 8 % PDB] + (db / 8) * 256; };
+    const uint32_t lane16 = 16u * lane;
     unsigned char *kwb = kbuf[wave];
     unsigned char *wbuf = vbuf[wave];
 
@@ -224,20 +247,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
         return ((uint32_t)(sb + (wave + kWaves * i) * kBlk) * W) * 2u;
     };
 
-    // One 32-key block of the current unit: scores, mask, online softmax,
-    // O^T += V^T P^T.
-    auto step = [&](const u32x4 (&kr)[VL], const u32x4 (&vr)[VLV], int i) {
+    // One 32-key block of the current unit: its K and V rows to the wave's
+    // LDS buffers, then scores, mask, online softmax, O^T += V^T P^T.
+    auto stage = [&](const u32x4 (&kr)[VL], const u32x4 (&vr)[VLV]) {
 #pragma unroll
-        for (int t = 0; t < VL; ++t) *reinterpret_cast<u32x4 *>(kwb + kw[t]) = kr[t];
+        for (int t = 0; t < VL; ++t) *reinterpret_cast<u32x4 *>(kwb + kw(t)) = kr[t];
 #pragma unroll
-        for (int t = 0; t < VLV; ++t) *reinterpret_cast<u32x4 *>(wbuf + vw[t]) = vr[t];
+        for (int t = 0; t < VLV; ++t) *reinterpret_cast<u32x4 *>(wbuf + vw(t)) = vr[t];
+    };
+    auto compute = [&](int i) {
         f32x4 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(kwb + kb * 16 * ROWB + krd[ks]);
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(kwb + kb * 16 * ROWB + krd(ks));
                 s[kb] = Mma<T>::run(__builtin_bit_cast(vec8, a), qop[ks], s[kb]);
             }
         }
@@ -271,12 +296,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             oacc[db] *= alpha;
-            const unsigned char *p = wbuf + vrd[db];
+            const unsigned char *p = wbuf + vrd(db);
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * ROWBV));
             const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             oacc[db] = Mma<T>::run(a, pb, oacc[db]);
         }
+    };
+    auto step = [&](const u32x4 (&kr)[VL], const u32x4 (&vr)[VLV], int i) {
+        stage(kr, vr);
+        compute(i);
     };
 
     // Persistent loop over units.  Within a unit the loop is double-buffered
@@ -284,10 +313,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
     // block's partner load fetches the next unit's first block and its Q is
     // loaded before the current unit's epilogue, so consecutive units stream
     // without a gap.
-    u32x4 kA[VL], vA[VLV], kB[VL], vB[VLV];
+    constexpr bool kSingle = single_set<D, DV>();
+    u32x4 kA[VL], vA[VLV], kB[kSingle ? 1 : VL], vB[kSingle ? 1 : VLV];
     auto load = [&](u32x4 (&kr)[VL], u32x4 (&vr)[VLV], __amdgpu_buffer_rsrc_t ks,
                     __amdgpu_buffer_rsrc_t vs, bool ok, int sb, int i) {
-        load_block<VL, VLV>(kr, vr, ks, vs, ok, block_base(sb, i, D), block_base(sb, i, DV), gofs, gofv);
+        load_block<VL, VLV>(kr, vr, ks, vs, ok, block_base(sb, i, D), block_base(sb, i, DV), lane16);
     };
     load(kA, vA, krs, vrs, 0 < mine, seg_begin, 0);
     for (;;) {
@@ -302,14 +332,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_segment_mfma_kernel(
         l = 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < mine; i += 2) {
-            load(kB, vB, krs, vrs, i + 1 < mine, seg_begin, i + 1);
-            step(kA, vA, i);
-            if (i + 2 < mine)
-                load(kA, vA, krs, vrs, true, seg_begin, i + 2);
-            else
-                load(kA, vA, nkrs, nvrs, nfirst, nbegin, 0);
-            if (i + 1 < mine) step(kB, vB, i + 1);
+        if constexpr (kSingle) {
+            for (int i = 0; i < mine; ++i) {
+                stage(kA, vA);
+                if (i + 1 < mine)
+                    load(kA, vA, krs, vrs, true, seg_begin, i + 1);
+                else
+                    load(kA, vA, nkrs, nvrs, nfirst, nbegin, 0);
+                compute(i);
+            }
+        } else {
+            for (int i = 0; i < mine; i += 2) {
+                load(kB, vB, krs, vrs, i + 1 < mine, seg_begin, i + 1);
+                step(kA, vA, i);
+                if (i + 2 < mine)
+                    load(kA, vA, krs, vrs, true, seg_begin, i + 2);
+                else
+                    load(kA, vA, nkrs, nvrs, nfirst, nbegin, 0);
+                if (i + 1 < mine) step(kB, vB, i + 1);
+            }
         }
         if (mine == 0) load(kA, vA, nkrs, nvrs, nfirst, nbegin, 0);
         vec8 qnext[KS];
@@ -405,11 +446,15 @@ hipError_t launch_typed(const DecodeArgs &d) {
 
 template <typename T, int D>
 hipError_t launch_dv(const DecodeArgs &d) {
-    switch (d.a.dv) {
-        case 32: return launch_typed<T, D, 32>(d);
-        case 64: return launch_typed<T, D, 64>(d);
-        case 128: return launch_typed<T, D, 128>(d);
-        default: return hipErrorInvalidValue;
+    if constexpr (D == 256) {
+        return d.a.dv == 256 ? launch_typed<T, 256, 256>(d) : hipErrorInvalidValue;
+    } else {
+        switch (d.a.dv) {
+            case 32: return launch_typed<T, D, 32>(d);
+            case 64: return launch_typed<T, D, 64>(d);
+            case 128: return launch_typed<T, D, 128>(d);
+            default: return hipErrorInvalidValue;
+        }
     }
 }
 
@@ -419,6 +464,7 @@ hipError_t launch_dim(const DecodeArgs &d) {
         case 32: return launch_dv<T, 32>(d);
         case 64: return launch_dv<T, 64>(d);
         case 128: return launch_dv<T, 128>(d);
+        case 256: return launch_dv<T, 256>(d);
         default: return hipErrorInvalidValue;
     }
 }

@@ -121,7 +121,7 @@ def test_gqa_many_rows_per_group(d):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("G,N,Nk,splits,causal", [
     (4, 1, 1000, 16, False),    # one 16-row tile, 4 rows used
     (16, 1, 95, 7, True),       # a full tile; ragged last block of 32 keys
@@ -143,6 +143,14 @@ def test_gqa_matrix_core_shapes(dtype, d, G, N, Nk, splits, causal):
 def test_gqa_matrix_core_unequal_dims(dtype, d, dv, G, N, Nk, splits, causal):
     # K rows of d and V rows of dv elements on the matrix-core segment kernel
     _run_gqa(1, 2, G, N, Nk, d, dtype, causal, splits, seed=G + N + d + dv, dv=dv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("splits", [64, 0])
+def test_gqa_d256_several_units_per_workgroup(dtype, splits):
+    # d = dv = 256 with 64 splits: 2048 (segment, head, tile) units for at
+    # most 256 resident workgroups, so each walks several units in a row
+    _run_gqa(4, 8, 4, 1, 6000, 256, dtype, True, splits, seed=31)
 
 
 def test_gqa_large_scores():
