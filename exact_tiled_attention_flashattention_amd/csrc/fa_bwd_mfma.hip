@@ -227,11 +227,18 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         used[t] = cwave < CHQ + CHO;
         isdo[t] = cwave >= CHQ;
         if constexpr (D == DV) {   // one layout for both tensors
-            const int ch = cidx % CHQ;
+            // chunk (t kThreads + tid) mod CHQ: the part from t is zero or a
+            // whole number of 16-row swizzle periods, so the offsets are
+            // t = 0's plus a constant (fewer registers at d = 256)
+            static_assert(CHQ <= kThreads ? kThreads % CHQ == 0
+                                          : CHQ % kThreads == 0 && (kThreads / CPRQ) % 16 == 0,
+                          "chunk offsets periodic in t");
+            const int ch = tid % CHQ;
             const int row = ch / CPRQ, cc = ch % CPRQ;
-            gofs[t] = ((uint32_t)row * D + cc * 8) * 2u;
-            wA[t] = row * ROWQ + ((cc ^ kswz<D>(row)) * 16);
-            wT[t] = row * ROWQ + (((2 * cc) ^ vswz<D>(row)) * 8);
+            const uint32_t add = (uint32_t)(((t * kThreads) % CHQ) / CPRQ) * ROWQ;
+            gofs[t] = ((uint32_t)row * D + cc * 8) * 2u + add;
+            wA[t] = row * ROWQ + ((cc ^ kswz<D>(row)) * 16) + add;
+            wT[t] = row * ROWQ + (((2 * cc) ^ vswz<D>(row)) * 8) + add;
             continue;
         }
         gofs[t] = wA[t] = wT[t] = 0;
@@ -276,9 +283,12 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
     // until it is stored to LDS stage x % 2 at the end of step x - 1.  The
     // step's (LSE log2 e, D) pairs are fetched the same way (bounds-checked:
     // rows past N read 0; wave 0 stores them), so that nothing waits on the
-    // loads just issued.
+    // loads just issued.  Where the dK and dV accumulators leave no room for
+    // two register sets (d + dv >= 384) steps are fetched one ahead through
+    // one set, which is stored to LDS and then refilled after each barrier.
+    constexpr bool kOneSet = D + DV >= 384;
     const auto wrs = make_rsrc(Wh, (uint32_t)N * 8u);
-    u32x4 regs0[NL], regs1[NL];
+    u32x4 regs0[NL], regs1[kOneSet ? 1 : NL];
     float vl0 = 0.f, vd0 = 0.f, vl1 = 0.f, vd1 = 0.f;
     auto load_step = [&](u32x4 (&rg)[NL], float &vl, float &vd, int s) {   // global -> registers
         const uint32_t baseq = (uint32_t)((s0 + s) * QS) * D * 2u;
@@ -396,7 +406,8 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
         load_step(regs0, vl0, vd0, 0);
         store_step(regs0, vl0, vd0, 0, 0);
     }
-    load_step(regs1, vl1, vd1, 1);
+    if constexpr (kOneSet) load_step(regs0, vl0, vd0, 1);
+    else load_step(regs1, vl1, vd1, 1);
     // Re-define the K^T and V^T operands (landed by now) so that the step
     // loop carries no dependence on their loads: it would otherwise wait on
     // the vector-memory counter, and so on the steps' own prefetch loads.
@@ -405,16 +416,30 @@ __global__ __launch_bounds__(kThreads, (bwd_waves_per_simd<D, DV>())) void bwd_d
 #pragma unroll
     for (int ks = 0; ks < KSV; ++ks) asm volatile("" : "+v"(vop[ks]));
     __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-        load_step(regs0, vl0, vd0, s + 2);
-        compute(s, 0);
-        if (s + 1 < nsteps) store_step(regs1, vl1, vd1, s + 1, 1);
-        __syncthreads();
-        if (s + 1 >= nsteps) break;
-        load_step(regs1, vl1, vd1, s + 3);
-        compute(s + 1, 1);
-        if (s + 2 < nsteps) store_step(regs0, vl0, vd0, s + 2, 0);
-        __syncthreads();
+    if constexpr (kOneSet) {
+        for (int s = 0; s < nsteps; s += 2) {
+            compute(s, 0);
+            if (s + 1 < nsteps) store_step(regs0, vl0, vd0, s + 1, 1);
+            __syncthreads();
+            load_step(regs0, vl0, vd0, s + 2);
+            if (s + 1 >= nsteps) break;
+            compute(s + 1, 1);
+            if (s + 2 < nsteps) store_step(regs0, vl0, vd0, s + 2, 0);
+            __syncthreads();
+            load_step(regs0, vl0, vd0, s + 3);
+        }
+    } else {
+        for (int s = 0; s < nsteps; s += 2) {
+            load_step(regs0, vl0, vd0, s + 2);
+            compute(s, 0);
+            if (s + 1 < nsteps) store_step(regs1, vl1, vd1, s + 1, 1);
+            __syncthreads();
+            if (s + 1 >= nsteps) break;
+            load_step(regs1, vl1, vd1, s + 3);
+            compute(s + 1, 1);
+            if (s + 2 < nsteps) store_step(regs0, vl0, vd0, s + 2, 0);
+            __syncthreads();
+        }
     }
 
     // dK^T, dV^T result blocks: lane holds columns 16 db + 4g + r of `key`.
