@@ -273,9 +273,8 @@ def summarize_trace(directory: str) -> None:
         f"decode_splitkv_gqa_{GQA_WORKLOAD}.txt": ("decode_segment_mfma_kernel",
                                                    ("decode_segment_mfma_kernel",
                                                     "decode_merge_kernel"), gqa_cmd),
-        f"bwd_mfma_{PREFILL}.txt": ("bwd_dq_mfma_kernel",
-                                    ("bwd_dkdv_mfma", "bwd_dq_mfma_kernel",
-                                     "bwd_dot_kernel"), bwd_cmd),
+        f"bwd_mfma_{PREFILL}.txt": ("bwd_dq_mfma",
+                                    ("bwd_dkdv_mfma", "bwd_dq_mfma", "bwd_dot_kernel"), bwd_cmd),
     }
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for fname, (primary, keys, cmd) in groups.items():
@@ -473,7 +472,7 @@ def bench_bwd(args, torch, fa, si, dev) -> int:
         "data": "synthetic (seeded torch Philox draws on the GPU)",
         "config": {"workload": PREFILL + " (fa_bwd)", "B": s.B, "H": s.H, "N": s.N, "Nk": s.Nk,
                    "d": s.d, "causal": True},
-        "roofline": {"kernel": "bwd_dq_mfma_kernel + bwd_dkdv_mfma32_kernel",
+        "roofline": {"kernel": "bwd_dq_mfma32_kernel + bwd_dkdv_mfma32_kernel",
                      "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "avg_launch_us": round(avg_s * 1e6, 2), "min_launch_us": round(min(ms) * 1e3, 2),

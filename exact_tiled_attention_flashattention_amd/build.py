@@ -20,12 +20,12 @@ LIBRARY = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd_rowwise.hip", "fa_fwd_mfma.hip", "fa_fwd_mfma_wide.hip", "fa_decode.hip",
            "fa_decode_mfma.hip", "fa_bwd.hip", "fa_bwd_mfma.hip",
-           "fa_fwd_mfma_generic.hip", "fa_bwd_mfma32.hip"]
+           "fa_fwd_mfma_generic.hip", "fa_bwd_mfma32.hip", "fa_bwd_dq_mfma32.hip"]
 # A second library, libfa_serial.so, differs only in the SERIAL_SOURCES, built
 # with FA_SERIAL_COPIES=1: every copy into LDS is waited for, between
 # barriers, before it is read.  Its results must equal libfa.so's bit for
 # bit (a race check of the staging); only the tests load it.
-SERIAL_SOURCES = ["fa_fwd_mfma_wide.hip", "fa_bwd_mfma32.hip"]
+SERIAL_SOURCES = ["fa_fwd_mfma_wide.hip", "fa_bwd_mfma32.hip", "fa_bwd_dq_mfma32.hip"]
 SERIAL_LIBRARY = os.path.join(PKG, "libfa_serial.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

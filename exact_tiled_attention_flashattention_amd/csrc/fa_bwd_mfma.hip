@@ -696,13 +696,18 @@ hipError_t launch2(const BwdArgs &b) {
     const float c = a.scale * kLog2e;
     const int off_c = a.causal ? (int)(a.Nk - a.N) : (int)a.Nk;
     // dQ first: it also writes the (LSE log2 e, D) pairs the dK/dV kernels read.
-    const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
-    hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV>), gq, dim3(kThreads), 0, a.stream,
-                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
-                       static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
-                       static_cast<const T *>(a.o), b.Dsum, static_cast<T *>(b.dq), (int)a.N,
-                       (int)a.Nk, off_c, c, a.scale, (int)heads);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (bwd_dq_mfma32_preferred(b)) {
+        e = launch_bwd_dq_mfma32(b);
+    } else {
+        const dim3 gq((unsigned)((a.N + kWaves * 16 - 1) / (kWaves * 16)) * heads);
+        hipLaunchKernelGGL((bwd_dq_mfma_kernel<T, D, DV>), gq, dim3(kThreads), 0, a.stream,
+                           static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                           static_cast<const T *>(a.v), a.lse, static_cast<const T *>(b.dout),
+                           static_cast<const T *>(a.o), b.Dsum, static_cast<T *>(b.dq), (int)a.N,
+                           (int)a.Nk, off_c, c, a.scale, (int)heads);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     if (bwd_dkdv_mfma32_preferred(b)) return launch_bwd_dkdv_mfma32(b);
     const dim3 gk((unsigned)((a.Nk + kWaves * 16 - 1) / (kWaves * 16)) * heads);

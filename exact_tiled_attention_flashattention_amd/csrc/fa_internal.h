@@ -91,5 +91,12 @@ hipError_t launch_bwd_mfma(const BwdArgs &b);
 bool bwd_dkdv_mfma32_supported(int dtype, int64_t d, int64_t dv);
 bool bwd_dkdv_mfma32_preferred(const BwdArgs &b);
 hipError_t launch_bwd_dkdv_mfma32(const BwdArgs &b);
+// dQ kernel on the 32x32x16 instruction (fa_bwd_dq_mfma32.hip): bf16/fp16,
+// d = dv = 64; like the dQ kernel of fa_bwd_mfma.hip it also writes the
+// (LSE log2 e, D) pairs.  _preferred: the shapes where it is the faster dQ
+// kernel.
+bool bwd_dq_mfma32_supported(int dtype, int64_t d, int64_t dv);
+bool bwd_dq_mfma32_preferred(const BwdArgs &b);
+hipError_t launch_bwd_dq_mfma32(const BwdArgs &b);
 
 }  // namespace fa

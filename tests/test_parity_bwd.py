@@ -92,11 +92,13 @@ def test_prefill_b64_h16_n1024_d64_all_heads():
     log(f"  bwd full-size: {s.B * s.H}/{s.B * s.H} heads compared element by element")
 
 
-@pytest.mark.parametrize("B,H,N,Nk,causal", [(8, 16, 1024, 1024, False), (5, 7, 1800, 1900, True)])
+@pytest.mark.parametrize("B,H,N,Nk,causal", [(8, 16, 1024, 1024, False), (5, 7, 1800, 1900, True),
+                                              (8, 16, 2100, 1900, True)])
 def test_several_blocks_per_workgroup_all_heads(B, H, N, Nk, causal):
-    """Shapes with more 256-key blocks than the GPU holds workgroups at once:
-    under the mask one workgroup of the d = 64 dK/dV kernel walks several
-    pairs of blocks (here with a head count that is not a multiple of 8),
+    """Shapes with more 256-key (256-row) blocks than the GPU holds
+    workgroups at once: under the mask one workgroup of the d = 64 dK/dV and
+    dQ kernels walks several pairs of blocks (a head count that is not a
+    multiple of 8 in the second case; rows that see no key in the third),
     without it each block has a workgroup of its own.  Every element of the
     gradients of every head against the oracle."""
     q, k, v, dout = _inputs(B, H, N, Nk, 64, "bf16", seed=N + Nk)

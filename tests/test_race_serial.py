@@ -86,6 +86,7 @@ BWD_CASES = [
     # during the last steps of the one before
     (8, 16, 2048, 2048, True),      # two pairs per workgroup
     (5, 7, 1800, 1900, True),       # head count not a multiple of 8, ragged
+    (8, 16, 2100, 1900, True),      # N > Nk: rows that see no key, several row blocks each
     (8, 16, 1024, 1024, False),     # unmasked: 512 blocks, one per workgroup
 ]
 
