@@ -346,9 +346,62 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         }
     };
 
+    // A step whose 64 keys every row of the wave sees (the common case off
+    // the diagonal): both sub-blocks' products S^T and dP^T are issued
+    // before either's exponentials, in one straight-line block, so that the
+    // second sub-block's products run on the matrix cores while the first
+    // one's vector work issues.
+    auto full_step = [&](int stage) __attribute__((always_inline)) {
+        vec8 ka[NSB][KS], va[NSB][KSV];
+        f32x16 S[NSB], dP[NSB];
+#pragma unroll
+        for (int b = 0; b < NSB; ++b) {
+            const unsigned char *sk = sbuf + stage * TK + b * kSB * ROWK;
+            const unsigned char *sv = sbuf + stage * TV + b * kSB * ROWV;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ka[b][ks] = *reinterpret_cast<const vec8 *>(sk + ak[ks]);
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks) va[b][ks] = *reinterpret_cast<const vec8 *>(sv + av[ks]);
+        }
+#pragma unroll
+        for (int b = 0; b < NSB; ++b) {
+            S[b] = f32x16{};
+            dP[b] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < (KS > KSV ? KS : KSV); ++ks) {
+                if (ks < KS) S[b] = Mfma<T>::run(ka[b][ks], qop[ks], S[b]);
+                if (ks < KSV) dP[b] = Mfma<T>::run(va[b][ks], dop[ks], dP[b]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NSB; ++b) {
+            const unsigned char *sk = sbuf + stage * TK + b * kSB * ROWK;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(S[b][r], c, -lse2));
+                dP[b][r] = p * (dP[b][r] - Drow);
+            }
+#pragma unroll
+            for (int kk = 0; kk < kSB / 16; ++kk) {
+                f32x8 df;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) df[e] = dP[b][8 * kk + e];
+                const vec8 db8 = __builtin_convertvector(df, vec8);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    dqa[db] = Mfma<T>::run(tr_read(sk + kk * 16 * ROWK + tk[db], ROWK), db8, dqa[db]);
+            }
+        }
+    };
+
     auto compute = [&](int s, int stage) __attribute__((always_inline)) {
-        sub(s * KST, std::integral_constant<int, 0>{}, stage);
-        if constexpr (NSB == 2) sub(s * KST + kSB, std::integral_constant<int, 1>{}, stage);
+        const int j0 = s * KST;
+        if (NSB == 2 && qw0 < N && j0 + KST <= Nk && j0 + KST - 1 <= off_c + qw0) {
+            full_step(stage);
+        } else {
+            sub(j0, std::integral_constant<int, 0>{}, stage);
+            if constexpr (NSB == 2) sub(j0 + kSB, std::integral_constant<int, 1>{}, stage);
+        }
     };
 
     // dQ = scale (dQ^T)^T of an item leaves through the wave's slice of obuf:
