@@ -37,6 +37,7 @@ import itertools
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -74,14 +75,13 @@ def decode_bytes(s) -> int:
     return (s.B * s.H * (2 * s.Nk * s.d * e + s.N * s.d * e + s.N * s.dv * e + s.N * 4))
 
 
-COMMON_SRCS = [os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc", n)
-               for n in ("fa_device.h", "fa_internal.h")]
-
-
 def source_hash(path: str) -> str:
-    """Hash of a kernel source together with the headers it includes."""
+    """Hash of a kernel source together with the library headers it includes."""
+    csrc = os.path.dirname(path)
+    with open(path) as f:
+        local = re.findall(r'^#include "([^"]+)"', f.read(), re.M)
     h = hashlib.sha256()
-    for p in [path, *COMMON_SRCS]:
+    for p in [path, *sorted(os.path.join(csrc, n) for n in local)]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
