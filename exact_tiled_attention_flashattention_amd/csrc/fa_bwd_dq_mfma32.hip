@@ -1,6 +1,6 @@
 // fa_bwd_dq_mfma32.hip -- the dQ half of the attention backward on the
 // CDNA4 32x32x16 matrix-core instruction (bf16/fp16 inputs, fp32
-// accumulation), d = dv = 64.
+// accumulation), d = dv in {64, 128}.
 //
 // Method: CS349E Lecture 11 "flash_lab.py", section 3 (flash_bwd, the
 // FlashAttention-2 backward), the query-block side: a block of query rows
@@ -18,7 +18,8 @@
 // rows of one head at a time, 32 per wave as the columns of 32x32 blocks;
 // two waves per SIMD.  The wave's Q and dO rows are B operands held in
 // registers for the whole block, and its rows' L2 and D one register each.
-// The walk goes over the keys in steps of 64 (two 32-key sub-blocks):
+// The walk goes over the keys in steps of 64 (two 32-key sub-blocks; one at
+// d = 128, where three stages of two would not fit in LDS):
 //  * S^T = K Q^T and dP^T = V dO^T: K and V are A operands read row-major
 //    from LDS; the 32x32 results give each lane one query row (lane % 32)
 //    and 16 of the sub-block's keys, 8 (r/4) + 4h + r%4 for register r
@@ -67,7 +68,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQW = 32;                  // query rows per wave
 constexpr int kBQ = kWaves * kQW;        // query rows per workgroup
 constexpr int kSB = 32;                  // keys per sub-block (one 32x32 product)
-constexpr int KST = 64;                  // keys per step (two sub-blocks)
 
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_mfma32_kernel(
@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     float *__restrict__ ws, T *__restrict__ dq, int N, int Nk, int off_c, float c, float scale,
     int heads, int paired) {
     typedef typename Mfma<T>::vec vec8;
-    static_assert(D == 64 && DV == 64, "(d, dv)");
+    static_assert((D == 64 || D == 128) && DV == D, "(d, dv)");
+    constexpr int KST = D == 64 ? 64 : 32;   // keys per step
     constexpr int KS = D / 16;               // 16-wide contraction steps of S^T (over d)
     constexpr int KSV = DV / 16;             // ... of dP^T (over dv)
     constexpr int DB = D / 32;               // 32-row blocks of dQ^T
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         const int base = x == 0 ? OKA : x == 1 ? OKT : OVA;
         const int slot = part * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
-        const int src = tr ? ((2 * pc) ^ vswz<64>(row)) / 2 : pc ^ kswz<64>(row);
+        const int src = tr ? ((2 * pc) ^ vswz<D>(row)) / 2 : pc ^ kswz<D>(row);
         goff[t] = ((uint32_t)row * W + src * 8) * 2u;
         loff[t] = base + part * 1024;
     }
@@ -576,26 +577,32 @@ hipError_t launch(const BwdArgs &b) {
 }  // namespace
 
 bool bwd_dq_mfma32_supported(int dtype, int64_t d, int64_t dv) {
-    return (dtype == kBF16 || dtype == kF16) && d == 64 && dv == 64;
+    return (dtype == kBF16 || dtype == kF16) && d == dv && (d == 64 || d == 128);
 }
 
 // Measured against the 16x16 dQ kernel of fa_bwd_mfma.hip (whole fa_bwd,
-// d = 64, bf16, paired HIP-event timings): 3.7% faster at causal
+// bf16, paired HIP-event timings).  d = 64: 3.7% faster at causal
 // B64 x H16 x 1024 and 4-5% at causal 2048 to 8192 rows, level or 1% slower
 // at causal 512 and 1000 rows, slower below one block per resident
 // workgroup (B1 x H16 x 1024: 56 against 47 us) and without the mask at
-// 1024 rows (1124 against 1086 us).
+// 1024 rows (1124 against 1086 us).  d = 128: 8-12% faster on every
+// measured shape with at least one block per resident workgroup, with and
+// without the mask, 512 to 8192 rows.
 bool bwd_dq_mfma32_preferred(const BwdArgs &b) {
     const FwdArgs &a = b.a;
-    if (!bwd_dq_mfma32_supported(a.dtype, a.d, a.dv) || !a.causal || a.N < 1024) return false;
-    const int resident = a.dtype == kBF16 ? resident_workgroups<bf16_t, 64, 64>()
-                                          : resident_workgroups<f16_t, 64, 64>();
+    if (!bwd_dq_mfma32_supported(a.dtype, a.d, a.dv)) return false;
+    if (a.d == 64 && (!a.causal || a.N < 1024)) return false;
+    const int resident = a.d == 64 ? (a.dtype == kBF16 ? resident_workgroups<bf16_t, 64, 64>()
+                                                       : resident_workgroups<f16_t, 64, 64>())
+                                   : (a.dtype == kBF16 ? resident_workgroups<bf16_t, 128, 128>()
+                                                       : resident_workgroups<f16_t, 128, 128>());
     return a.B * a.H * ((a.N + kBQ - 1) / kBQ) >= resident;
 }
 
 hipError_t launch_bwd_dq_mfma32(const BwdArgs &b) {
     if (!bwd_dq_mfma32_supported(b.a.dtype, b.a.d, b.a.dv)) return hipErrorInvalidValue;
-    return b.a.dtype == kBF16 ? launch<bf16_t, 64, 64>(b) : launch<f16_t, 64, 64>(b);
+    if (b.a.d == 64) return b.a.dtype == kBF16 ? launch<bf16_t, 64, 64>(b) : launch<f16_t, 64, 64>(b);
+    return b.a.dtype == kBF16 ? launch<bf16_t, 128, 128>(b) : launch<f16_t, 128, 128>(b);
 }
 
 }  // namespace fa

@@ -110,3 +110,21 @@ def test_several_blocks_per_workgroup_all_heads(B, H, N, Nk, causal):
     torch.cuda.synchronize()
     ref = oracle_bwd_on(q, k, v, dout, causal, scale)
     compare_grads((dq, dk, dv), ref, "bf16", f"bwd B={B} H={H} N={N} Nk={Nk}")
+
+
+@pytest.mark.parametrize("N,Nk,causal", [(1100, 1200, True), (1024, 1000, False)])
+def test_d128_row_blocks_all_heads(N, Nk, causal):
+    """d = dv = 128 with more 256-row blocks than resident workgroups,
+    N != Nk (ragged): the 32x32 dQ kernel with one 32-key sub-block per
+    step (a persistent walk of pairs under the mask).  Every element of
+    every head against the oracle."""
+    B, H = 8, 16
+    q, k, v, dout = _inputs(B, H, N, Nk, 128, "bf16", seed=N + Nk + 128)
+    scale = default_scale(128)
+    log(f"fa_bwd d=128 B={B} H={H} N={N} Nk={Nk} causal={causal}")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle_bwd_on(q, k, v, dout, causal, scale)
+    compare_grads((dq, dk, dv), ref, "bf16", f"bwd d=128 B={B} H={H} N={N} Nk={Nk} causal={causal}")
