@@ -1,6 +1,6 @@
 // fa_bwd_dq_mfma32.hip -- the dQ half of the attention backward on the
 // CDNA4 32x32x16 matrix-core instruction (bf16/fp16 inputs, fp32
-// accumulation), d = dv in {64, 128}.
+// accumulation), d = dv in {64, 128} and d = 64 with dv = 128.
 //
 // Method: CS349E Lecture 11 "flash_lab.py", section 3 (flash_bwd, the
 // FlashAttention-2 backward), the query-block side: a block of query rows
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     float *__restrict__ ws, T *__restrict__ dq, int N, int Nk, int off_c, float c, float scale,
     int heads, int paired) {
     typedef typename Mfma<T>::vec vec8;
-    static_assert((D == 64 || D == 128) && DV == D, "(d, dv)");
+    static_assert(((D == 64 || D == 128) && DV == D) || (D == 64 && DV == 128), "(d, dv)");
     constexpr int KST = D == 64 ? 64 : 32;   // keys per step
     constexpr int KS = D / 16;               // 16-wide contraction steps of S^T (over d)
     constexpr int KSV = DV / 16;             // ... of dP^T (over dv)
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         const int base = x == 0 ? OKA : x == 1 ? OKT : OVA;
         const int slot = part * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
-        const int src = tr ? ((2 * pc) ^ vswz<D>(row)) / 2 : pc ^ kswz<D>(row);
+        const int src = tr ? ((2 * pc) ^ vswz<D>(row)) / 2 : pc ^ (isk[t] ? kswz<D>(row) : kswz<DV>(row));
         goff[t] = ((uint32_t)row * W + src * 8) * 2u;
         loff[t] = base + part * 1024;
     }
@@ -577,7 +577,8 @@ hipError_t launch(const BwdArgs &b) {
 }  // namespace
 
 bool bwd_dq_mfma32_supported(int dtype, int64_t d, int64_t dv) {
-    return (dtype == kBF16 || dtype == kF16) && d == dv && (d == 64 || d == 128);
+    return (dtype == kBF16 || dtype == kF16) &&
+           ((d == dv && (d == 64 || d == 128)) || (d == 64 && dv == 128));
 }
 
 // Measured against the 16x16 dQ kernel of fa_bwd_mfma.hip (whole fa_bwd,
@@ -585,24 +586,27 @@ bool bwd_dq_mfma32_supported(int dtype, int64_t d, int64_t dv) {
 // B64 x H16 x 1024 and 4-5% at causal 2048 to 8192 rows, level or 1% slower
 // at causal 512 and 1000 rows, slower below one block per resident
 // workgroup (B1 x H16 x 1024: 56 against 47 us) and without the mask at
-// 1024 rows (1124 against 1086 us).  d = 128: 8-12% faster on every
-// measured shape with at least one block per resident workgroup, with and
-// without the mask, 512 to 8192 rows.
+// 1024 rows (1124 against 1086 us).  d = 128, and d = 64 with dv = 128:
+// 8-13% faster on every measured shape with at least one block per
+// resident workgroup, with and without the mask, 512 to 8192 rows.
 bool bwd_dq_mfma32_preferred(const BwdArgs &b) {
     const FwdArgs &a = b.a;
     if (!bwd_dq_mfma32_supported(a.dtype, a.d, a.dv)) return false;
-    if (a.d == 64 && (!a.causal || a.N < 1024)) return false;
-    const int resident = a.d == 64 ? (a.dtype == kBF16 ? resident_workgroups<bf16_t, 64, 64>()
-                                                       : resident_workgroups<f16_t, 64, 64>())
-                                   : (a.dtype == kBF16 ? resident_workgroups<bf16_t, 128, 128>()
-                                                       : resident_workgroups<f16_t, 128, 128>());
+    if (a.d == 64 && a.dv == 64 && (!a.causal || a.N < 1024)) return false;
+    const bool bf = a.dtype == kBF16;
+    const int resident =
+        a.d == 128   ? (bf ? resident_workgroups<bf16_t, 128, 128>() : resident_workgroups<f16_t, 128, 128>())
+        : a.dv == 128 ? (bf ? resident_workgroups<bf16_t, 64, 128>() : resident_workgroups<f16_t, 64, 128>())
+                      : (bf ? resident_workgroups<bf16_t, 64, 64>() : resident_workgroups<f16_t, 64, 64>());
     return a.B * a.H * ((a.N + kBQ - 1) / kBQ) >= resident;
 }
 
 hipError_t launch_bwd_dq_mfma32(const BwdArgs &b) {
     if (!bwd_dq_mfma32_supported(b.a.dtype, b.a.d, b.a.dv)) return hipErrorInvalidValue;
-    if (b.a.d == 64) return b.a.dtype == kBF16 ? launch<bf16_t, 64, 64>(b) : launch<f16_t, 64, 64>(b);
-    return b.a.dtype == kBF16 ? launch<bf16_t, 128, 128>(b) : launch<f16_t, 128, 128>(b);
+    const bool bf = b.a.dtype == kBF16;
+    if (b.a.d == 128) return bf ? launch<bf16_t, 128, 128>(b) : launch<f16_t, 128, 128>(b);
+    if (b.a.dv == 128) return bf ? launch<bf16_t, 64, 128>(b) : launch<f16_t, 64, 128>(b);
+    return bf ? launch<bf16_t, 64, 64>(b) : launch<f16_t, 64, 64>(b);
 }
 
 }  // namespace fa

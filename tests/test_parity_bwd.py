@@ -128,3 +128,21 @@ def test_d128_row_blocks_all_heads(N, Nk, causal):
     torch.cuda.synchronize()
     ref = oracle_bwd_on(q, k, v, dout, causal, scale)
     compare_grads((dq, dk, dv), ref, "bf16", f"bwd d=128 B={B} H={H} N={N} Nk={Nk} causal={causal}")
+
+
+@pytest.mark.parametrize("N,Nk,causal", [(1100, 1200, True), (1024, 1000, False)])
+def test_d64_dv128_row_blocks_all_heads(N, Nk, causal):
+    """d = 64 with dv = 128, more 256-row blocks than resident workgroups,
+    N != Nk: the 32x32 dQ kernel with V rows twice as long as K rows.  Every
+    element of every head against the oracle."""
+    B, H, d, dv = 8, 16, 64, 128
+    q, k, v = make_inputs(B, H, N, Nk, d, dv, "bf16", 71)
+    dout, _, _ = make_inputs(B, H, N, 1, dv, dv, "bf16", 72)
+    scale = default_scale(d)
+    log(f"fa_bwd d={d} dv={dv} B={B} H={H} N={N} Nk={Nk} causal={causal}")
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dvv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=scale, dq=dq, dk=dk, dv=dvv)
+    torch.cuda.synchronize()
+    ref = oracle_bwd_on(q, k, v, dout, causal, scale)
+    compare_grads((dq, dk, dvv), ref, "bf16", f"bwd d={d} dv={dv} B={B} H={H} N={N} Nk={Nk}")

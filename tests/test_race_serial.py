@@ -92,23 +92,25 @@ BWD_CASES = [
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("B,H,N,Nk,causal,d", [c + (64,) for c in BWD_CASES] + [
-    # d = 128: the 32x32 dQ kernel with one 32-key sub-block per step
-    (8, 16, 1100, 1200, True, 128),
+@pytest.mark.parametrize("B,H,N,Nk,causal,d,dv", [c + (64, 64) for c in BWD_CASES] + [
+    # the 32x32 dQ kernel at d = 128 (one 32-key sub-block per step) and at
+    # d = 64 with dv = 128
+    (8, 16, 1100, 1200, True, 128, 128),
+    (8, 16, 1100, 1200, True, 64, 128),
 ])
-def test_backward_pipelined_equals_serial_bitwise(dtype, B, H, N, Nk, causal, d):
+def test_backward_pipelined_equals_serial_bitwise(dtype, B, H, N, Nk, causal, d, dv):
     lib = _serial_lib()
-    q, k, v = make_inputs(B, H, N, Nk, d, d, dtype, seed=B + N + Nk)
-    dout, _, _ = make_inputs(B, H, N, 1, d, d, dtype, seed=N + 7)
+    q, k, v = make_inputs(B, H, N, Nk, d, dv, dtype, seed=B + N + Nk)
+    dout, _, _ = make_inputs(B, H, N, 1, dv, dv, dtype, seed=N + 7)
     scale = 0.125
-    log(f"bwd race check dtype={dtype} B={B} H={H} N={N} Nk={Nk} d={d} causal={causal}")
+    log(f"bwd race check dtype={dtype} B={B} H={H} N={N} Nk={Nk} d={d} dv={dv} causal={causal}")
     o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
     g1 = fa.bwd(q, k, v, o, lse, dout, causal=causal, scale=scale)
     g2 = [torch.full_like(t, float("nan")) for t in (q, k, v)]
     ws = torch.empty(fa.bwd_workspace_size(B, H, N), dtype=torch.uint8, device=q.device)
     st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), g2[0].data_ptr(), g2[1].data_ptr(), g2[2].data_ptr(),
-                    B, H, N, Nk, d, d, int(causal), scale, 2 if dtype == "bf16" else 1,
+                    B, H, N, Nk, d, dv, int(causal), scale, 2 if dtype == "bf16" else 1,
                     ws.data_ptr(), ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 0, fa.status_string(st)
     torch.cuda.synchronize()
