@@ -410,20 +410,8 @@ __global__ __launch_bounds__(kThreads, (single_set<D, DV>() ? 1 : 2)) void decod
 template <typename T, int D, int DV>
 int resident_workgroups() {
     static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int val = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-    if (val > 0) return val;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&decode_segment_mfma_kernel<T, D, DV>), kThreads,
-            0) != hipSuccess)
-        return 0;
-    val = cus * (per_cu > 0 ? per_cu : 1);
-    __atomic_store_n(&cache[dev], val, __ATOMIC_RELAXED);
-    return val;
+    return resident_workgroups_of(reinterpret_cast<const void *>(&decode_segment_mfma_kernel<T, D, DV>),
+                                  kThreads, cache);
 }
 
 template <typename T, int D, int DV>

@@ -535,20 +535,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
 template <typename T, int D, int DV, bool CAUSAL>
 int resident_workgroups() {
     static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-    if (v > 0) return v;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&fwd_mfma32_kernel<T, D, DV, CAUSAL>), kThreads, 0) !=
-        hipSuccess)
-        return 0;
-    v = cus * (per_cu > 0 ? per_cu : 1);
-    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
-    return v;
+    return resident_workgroups_of(reinterpret_cast<const void *>(&fwd_mfma32_kernel<T, D, DV, CAUSAL>),
+                                  kThreads, cache);
 }
 
 template <typename T, int D, int DV, bool CAUSAL>

@@ -10,6 +10,24 @@
 
 namespace fa {
 
+// Resident workgroups of one kernel on the current device: the CU count times
+// the workgroups of `threads` threads a CU holds at once.  Cached per device
+// in `cache` (one zero-initialised array per kernel); 0 if a query fails.
+inline int resident_workgroups_of(const void *kernel, int threads, int (&cache)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int val = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (val > 0) return val;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+        return 0;
+    val = cus * (per_cu > 0 ? per_cu : 1);
+    __atomic_store_n(&cache[dev], val, __ATOMIC_RELAXED);
+    return val;
+}
+
 enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 struct FwdArgs {
