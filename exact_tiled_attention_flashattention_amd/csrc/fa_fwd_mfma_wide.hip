@@ -41,7 +41,8 @@
 //    blocks of one head whose causal costs add up to a constant, numbered
 //    so that workgroups of one XCD share heads (K/V reuse in that L2).
 //  * At d = 64 the kernel needs 80 KiB of LDS and about 125 registers, so
-//    two workgroups share a CU (the launch bounds ask for two there).
+//    two workgroups share a CU (the launch bounds ask for four waves per
+//    SIMD there).
 //    Their items start and end at different times, and one workgroup's
 //    item boundary (Q and first tiles in flight, output stores) overlaps
 //    the other's tile loop.  That wins over the one-workgroup ping-pong
@@ -130,7 +131,9 @@ __device__ __forceinline__ Cursor next_item(Cursor cu, const Schedule &s) {
 
 
 template <typename T, int D, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_mfma32_kernel(
+// __launch_bounds__' second argument is the minimum number of waves per SIMD:
+// 4 (two workgroups per CU, at most 128 registers) at d = dv = 64, else 2.
+__global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_mfma32_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     T *__restrict__ o, float *__restrict__ lse, int N, int Nk, float c,
     int q_blocks, int n_items) {
@@ -203,8 +206,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
     // outstanding only what was issued after a recorded count (operations
     // complete in issue order).
     int issued = 0;
-    auto dma_k = [&](int head, int tile, int stage) __attribute__((always_inline)) {
-        const u32x4 kw = rsrc_words(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    auto k_words = [&](int head) __attribute__((always_inline)) {
+        return rsrc_words(k + (int64_t)head * Nk * D, (uint32_t)Nk * D * 2u);
+    };
+    auto v_words = [&](int head) __attribute__((always_inline)) {
+        return rsrc_words(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
+    };
+    auto dma_k_w = [&](const u32x4 &kw, int tile, int stage) __attribute__((always_inline)) {
         const uint32_t tile_off = (uint32_t)tile * kBC * D * 2u;
 #pragma unroll
         for (int t = 0; t < LPT; ++t)
@@ -212,14 +220,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
                       tile_off + koff[t]);
         issued += LPT;
     };
-    auto dma_v = [&](int head, int tile, int stage) __attribute__((always_inline)) {
-        const u32x4 vw = rsrc_words(v + (int64_t)head * Nk * DV, (uint32_t)Nk * DV * 2u);
+    auto dma_v_w = [&](const u32x4 &vw, int tile, int stage) __attribute__((always_inline)) {
         const uint32_t tile_off = (uint32_t)tile * kBC * DV * 2u;
 #pragma unroll
         for (int t = 0; t < LPTV; ++t)
             lds_dma16(vw, __builtin_amdgcn_readfirstlane(vlds + stage * TILEV + (t * kWaves + wave) * 1024),
                       tile_off + voff[t]);
         issued += LPTV;
+    };
+    auto dma_k = [&](int head, int tile, int stage) __attribute__((always_inline)) {
+        dma_k_w(k_words(head), tile, stage);
+    };
+    auto dma_v = [&](int head, int tile, int stage) __attribute__((always_inline)) {
+        dma_v_w(v_words(head), tile, stage);
     };
     // Q block of an item into qbuf, rows swizzled like K rows.
     auto dma_q = [&](int head, int qblk) __attribute__((always_inline)) {
@@ -314,7 +327,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
         constexpr int P = decltype(SP)::value;
         constexpr int NKB = decltype(NKBC)::value;
         const int j0 = j * kBC;
-        if (j0 + 32 * NKB > full_end) {
+        if (__builtin_expect(j0 + 32 * NKB > full_end, 0)) {
             const int t = lim - j0;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -327,10 +340,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
     // The running max m only moves when a row's tile max exceeds it by more
     // than 8 (base 2); otherwise the stale m is kept, so the probabilities
     // stay <= 2^8 and the accumulator needs no rescale.  The result is
-    // unchanged: O and l share the same m.  Returns the factor the output
-    // accumulator must be multiplied by (1 unless m moved); the multiply is
-    // left to the caller so that this code has no branch.
-    auto softmax = [&](auto SP, auto NKBC) __attribute__((always_inline)) -> float {
+    // unchanged: O and l share the same m.  When m moves, l and the output
+    // accumulator are multiplied by the correction factor (exactly 1 in the
+    // rows of the wave whose m stays).
+    auto softmax = [&](auto SP, auto NKBC) __attribute__((always_inline)) {
         constexpr int P = decltype(SP)::value;
         constexpr int NKB = decltype(NKBC)::value;
         float x = sb[P][0][0];
@@ -341,14 +354,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
         // The row's tile maximum exceeds m + 8 exactly when one of its two
         // lanes' maxima does: the row maximum (a lane exchange) is formed
         // only in the rare case that some row of the wave moves.
-        float a = 1.f;
-        if (__builtin_amdgcn_ballot_w64(x * c > m + 8.f)) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(x * c > m + 8.f) != 0, 0)) {
             const float mt = halves_max(x) * c;
             const bool need = mt > m + 8.f;
             const float m_new = need ? mt : m;
-            a = need ? fast_exp2(m - m_new) : 1.f;   // 0 when m = -inf < m_new
+            const float a = need ? fast_exp2(m - m_new) : 1.f;   // 0 when m = -inf < m_new
             l *= a;
             m = m_new;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= a;
         }
         const float m_use = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
@@ -358,13 +372,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
             for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(fmaf(sb[P][cc / 2][8 * (cc % 2) + e], c, -m_use));
             pb[cc] = __builtin_convertvector(pf, vec8);
             l = row_sum_pairs(pb[cc], l);
-        }
-        return a;
-    };
-    auto rescale = [&](const float a) __attribute__((always_inline)) {
-        if (__builtin_amdgcn_ballot_w64(a != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= a;
         }
     };
     // ---- schedule of the copies --------------------------------------------------
@@ -455,11 +462,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
                 barrier();
                 return;
             }
-            wait_pending(issued - mark);
+            // In the steady state the previous iteration issued exactly one
+            // K and one V tile: that count gets its own short path.
+            const int pend = issued - mark;
+            if (pend == LPT + LPTV) wait_vmcnt<LPT + LPTV>();
+            else wait_pending(pend);
             barrier();
             mark = issued;
-            if (j + KLEAD < ntiles) dma_k(head, j + KLEAD, (st + KLEAD) % 3);
-            if (j + 2 < ntiles) dma_v(head, j + 2, (st + 2) % 3);
+            static_assert(KLEAD == 2, "stage two ahead");
+            const int st2 = st == 0 ? 2 : st - 1;   // (st + 2) mod 3
+            if (__builtin_expect(j + 2 < ntiles, 1)) {
+                dma_k(head, j + KLEAD, st2);
+                dma_v(head, j + 2, st2);
+            }
             if (j == 0) prefetch_next();
         };
         // One computed tile: scores, mask, softmax, P V.
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 2 : 1) void fwd_m
             sync(j, st);
             scores(st, I0{}, NKBC);
             mask(j, I0{}, NKBC);
-            rescale(softmax(I0{}, NKBC));
+            softmax(I0{}, NKBC);
             accumulate(st, NKBC);
         };
         int j = 0, st = 0;
