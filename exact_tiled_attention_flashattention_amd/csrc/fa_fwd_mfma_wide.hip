@@ -525,18 +525,57 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
         const float lt = halves_sum(l);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const auto ors = make_rsrc(o + (int64_t)head * N * DV, (uint32_t)N * DV * 2u);
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        if constexpr (D == DV) {
+            // The wave's 32 x dv block goes through LDS and leaves as whole
+            // rows (16 bytes per lane, 1 KiB contiguous per instruction).
+            // Once every wave has passed the item's last barrier, only the
+            // stage of the last tile can still be read: the other two
+            // stages (st and st + 1) hold the 8 blocks, two per K or V
+            // tile.  Chunk c of row r sits at chunk c ^ oswz(r) (conflict
+            // free both ways); a wave reads back only what it wrote.
+            constexpr int RB = DV * 2;            // bytes per output row
+            constexpr int CPRO = RB / 16;         // 16-byte chunks per row
+            constexpr int RPI = 64 / CPRO;        // rows per store instruction
+            const int sidx = wave < 4 ? st : (st == 2 ? 0 : st + 1);
+            unsigned char *slot = ((wave / 2) % 2 == 0 ? kbuf[sidx] : vbuf[sidx]) + (wave % 2) * (kQW * RB);
+            auto oswz = [](int r) __attribute__((always_inline)) {
+                return DV == 64 ? (r >> 1) & 7 : r & 15;
+            };
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                typedef T t4 __attribute__((ext_vector_type(4)));
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                t4 out;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    t4 out;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * r4 + e] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ors,
-                                                      ((uint32_t)qi * DV + 32 * db + 8 * r4 + 4 * h) * 2u, 0, 0);
+                    for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * r4 + e] * inv);
+                    *reinterpret_cast<t4 *>(slot + n * RB + (((4 * db + r4) ^ oswz(n)) * 16) + 8 * h) = out;
+                }
+            // (the lane index is re-defined so that this address arithmetic
+            // is not hoisted into the tile loops)
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            const int rr = el / CPRO, cc = el % CPRO;
+#pragma unroll
+            for (int t = 0; t < kQW / RPI; ++t) {
+                const int r = t * RPI + rr;
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(slot + r * RB + ((cc ^ oswz(r)) * 16));
+                // Bounds-checked: rows past N fall outside the view and are dropped.
+                __builtin_amdgcn_raw_buffer_store_b128(val, ors, (int)(((uint32_t)(qw0 + r) * DV) * 2u + cc * 16), 0, 0);
             }
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    t4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][4 * r4 + e] * inv);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ors,
+                                                          ((uint32_t)qi * DV + 32 * db + 8 * r4 + 4 * h) * 2u, 0, 0);
+                }
+        }
         const auto lrs = make_rsrc(lse + (int64_t)head * N, (uint32_t)N * 4u);
         const float lv = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lv), lrs, h == 0 ? (uint32_t)qi * 4u : 0x80000000u, 0, 0);
