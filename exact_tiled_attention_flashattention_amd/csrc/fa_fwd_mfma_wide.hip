@@ -284,6 +284,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
     // ---- per-item state ----------------------------------------------------------
     vec8 qop[KS];
     float m, l;
+    float m8, neg_mu;   // m + 8 and -(m, or 0 while m = -inf), updated with m
     f32x16 oacc[DB];
     f32x16 sb[1][2];              // scores of the current tile: [32-key block]
     vec8 pb[CC];                  // probabilities of the current tile (B operands)
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 8 * (r / 4) + r % 4 > t) sb[P][kb][r] = -INFINITY;
+                    sb[P][kb][r] = 32 * kb + 8 * (r / 4) + r % 4 > t ? -INFINITY : sb[P][kb][r];
         }
     };
     // ---- online softmax of score buffer SP with lazy rescaling ---------------------
@@ -354,22 +355,23 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
         // The row's tile maximum exceeds m + 8 exactly when one of its two
         // lanes' maxima does: the row maximum (a lane exchange) is formed
         // only in the rare case that some row of the wave moves.
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(x * c > m + 8.f) != 0, 0)) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(x * c > m8) != 0, 0)) {
             const float mt = halves_max(x) * c;
-            const bool need = mt > m + 8.f;
+            const bool need = mt > m8;
             const float m_new = need ? mt : m;
             const float a = need ? fast_exp2(m - m_new) : 1.f;   // 0 when m = -inf < m_new
             l *= a;
             m = m_new;
+            m8 = m + 8.f;
+            neg_mu = -((m == -INFINITY) ? 0.f : m);
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= a;
         }
-        const float m_use = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
         for (int cc = 0; cc < CC * NKB / 2; ++cc) {
             f32x8 pf;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(fmaf(sb[P][cc / 2][8 * (cc % 2) + e], c, -m_use));
+            for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(fmaf(sb[P][cc / 2][8 * (cc % 2) + e], c, neg_mu));
             pb[cc] = __builtin_convertvector(pf, vec8);
             l = row_sum_pairs(pb[cc], l);
         }
@@ -411,6 +413,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
         const int qi = qw0 + n;
         lim = (CAUSAL ? min(Nk - 1, Nk - N + qi) : Nk - 1) - 4 * h;
         m = -INFINITY;
+        m8 = -INFINITY;
+        neg_mu = -0.f;
         l = 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
