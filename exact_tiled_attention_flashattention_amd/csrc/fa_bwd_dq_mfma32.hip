@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
             for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    if (8 * a + b > lim) dP[4 * a + b] = 0.f;
+                    dP[4 * a + b] = 8 * a + b > lim ? 0.f : dP[4 * a + b];
         }
 #pragma unroll
         for (int kk = 0; kk < kSB / 16; ++kk) {
