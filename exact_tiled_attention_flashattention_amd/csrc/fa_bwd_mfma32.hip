@@ -329,6 +329,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
             if (ks < KS) S = Mfma<T>::run(qa[ks], kop[ks], S);
             if (ks < KSV) dP = Mfma<T>::run(oa[ks], vop[ks], dP);
         }
+        // The scores of the keys a row does not see become -inf, so that
+        // their P = 2^(-inf) and dS = P (dP - D) are exactly 0 (dP and D are
+        // finite).  Register 4a + b is row 8a + 4h + b, which sees `key` iff
+        // 8a + b >= u.  Only a step that straddles the diagonal masks.
+        if (kw0 + kKW - 1 > off_c + i0) {
+            const int u = key - off_c - i0 - 4 * h;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    S[4 * a + b] = 8 * a + b < u ? -INFINITY : S[4 * a + b];
+        }
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -338,21 +350,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
                 S[r] = p;
                 dP[r] = p * (dP[r] - D4[a][b]);
             }
-        // P and dS of the keys a row does not see are set to 0 (after the
-        // arithmetic, whose values there are meaningless and may be inf or
-        // NaN).  Register 4a + b is row 8a + 4h + b, which sees `key` iff
-        // 8a + b + t >= 0.  Only a step that straddles the diagonal masks.
-        if (kw0 + kKW - 1 > off_c + i0) {
-            const int t = off_c + i0 + 4 * h - key;
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    if (8 * a + b + t < 0) {
-                        S[4 * a + b] = 0.f;
-                        dP[4 * a + b] = 0.f;
-                    }
-        }
 #pragma unroll
         for (int kk = 0; kk < kSB / 16; ++kk) {
             f32x8 pf, df;
