@@ -38,8 +38,10 @@
 // workgroups at once, the grid is persistent and a workgroup walks pairs of
 // blocks, k and nblk - 1 - k, whose steps add up to the same count for every
 // k; the copies of a block's first two steps are issued during the last two
-// steps of the block before, so only the operand loads of K and V are
-// exposed at a block's start.  Otherwise each block has a workgroup.
+// steps of the block before, and its K and V operands are loaded into a
+// second register set during the first step of the block before, so a
+// block starts without waiting on memory.  Otherwise each block has a
+// workgroup.
 // Under the causal mask (query i at position Nk - N + i) the walk starts at
 // the first row that sees the block's first key, a wave skips the steps in
 // which none of its keys is visible, and only steps that straddle the
@@ -246,8 +248,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // in branches: captured by reference, or stored on some paths only,
     // they would stay in memory)
     struct Counts {
-        int con, prev, nissued;
-    } ps = {0, 0, 0};
+        int con, prev, nissued, pf;
+    } ps = {0, 0, 0, 0};
     // Buffer resources of one head's Q, dO and (L2, D) pairs.
     struct Src {
         u32x4 qw, ow, lw;
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     };
 
     vec8 kop[KS], vop[KSV];
+    vec8 kon[KS], von[KSV];   // the next item's, fetched during the item's first step
     f32x16 dka[DBK], dva[DBV];
     int kw0 = 0, key = 0;
 
@@ -411,15 +414,35 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // the copies of the step two ahead in the stream, which is the next
     // item's step 0 or 1 near an item's end; before the barrier it waits
     // until only the copies issued after this step's are outstanding.  The
-    // next item's first two steps that were not fetched ahead, and its
-    // operands, are fetched when it starts, and waited for there.
-    auto wait_prev = [&](int prev) __attribute__((always_inline)) {
-        if (prev == 0) wait_vmcnt<0>();
-        else if (wave < NLD) wait_vmcnt<LPW + 1>();
-        else wait_vmcnt<LPW>();
+    // next item's first two steps that were not fetched ahead are fetched
+    // when it starts, and waited for there.  Its K and V operands are
+    // loaded in the first step of the item before (`pf`: NPF loads, issued
+    // before that step's copies, so they may stay outstanding through the
+    // next step's wait and have landed by the one after).  (Leaving the
+    // item before's output stores outstanding at an item's start as well
+    // measured slower.)
+    constexpr int NPF = KS + KSV;
+    auto wait_prev = [&](int prev, int pf) __attribute__((always_inline)) {
+        if (prev == 0) {
+            if (pf == 0) wait_vmcnt<0>();
+            else wait_vmcnt<NPF>();
+        } else if (pf == 0) {
+            if (wave < NLD) wait_vmcnt<LPW + 1>();
+            else wait_vmcnt<LPW>();
+        } else {
+            if (wave < NLD) wait_vmcnt<LPW + 1 + NPF>();
+            else wait_vmcnt<LPW + NPF>();
+        }
     };
-    auto start = [&](const Item &it) __attribute__((always_inline)) {
-        load_kv(it.head, it.j0, kop, vop);
+    auto start = [&](const Item &it, bool prefetched) __attribute__((always_inline)) {
+        if (prefetched) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kop[ks] = kon[ks];
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks) vop[ks] = von[ks];
+        } else {
+            load_kv(it.head, it.j0, kop, vop);
+        }
         wait_vmcnt<0>();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -436,12 +459,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         const Src w = src_of(cur.head);
         if (!kSerialCopies)
             for (int s = 0; s < 2 && s < cur.nsteps; ++s) issue(w, cur.s0, s, s);
-        start(cur);
+        start(cur, false);
     }
     for (;;) {
         const Item nxt = next_item(cur);
         const Src cw = src_of(cur.head);
         ps.prev = 0;
+        ps.pf = 0;
         ps.nissued = 0;   // steps of nxt already fetched
         kw0 = cur.j0 + wave * kKW;
         key = kw0 + n;
@@ -460,8 +484,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
                 wait_vmcnt<0>();
                 barrier();
             } else {
-                wait_prev(ps_.prev);
+                wait_prev(ps_.prev, ps_.pf);
                 barrier();
+                const bool pf = s == 0 && nxt_.head >= 0;
+                if (pf) {
+                    int hd = nxt_.head, j0n = nxt_.j0;
+                    asm volatile("" : "+s"(hd), "+s"(j0n));
+                    load_kv(hd, j0n, kon, von);
+                }
+                ps_.pf = pf ? 1 : 0;
                 const int jn = s + 2 - cur_.nsteps;   // >= 0: the next item's step
                 const bool ahead_next = jn >= 0 && nxt_.head >= 0 && jn == ps_.nissued && jn < nxt_.nsteps;
                 if (jn < 0) {
@@ -501,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         const Src nw = src_of(nxt.head);
         if (!kSerialCopies)
             for (int s = ps.nissued; s < 2 && s < nxt.nsteps; ++s) issue(nw, nxt.s0, s, (ps.con + s) % 3);
-        start(nxt);
+        start(nxt, !kSerialCopies && cur.nsteps > 0);
         cur = nxt;
     }
 }
