@@ -37,13 +37,15 @@
 //    and XOR-swizzled per row (16-byte chunks for K, 64-byte groups for V)
 //    so that the operand reads are free of bank conflicts.  The Q block of
 //    the next item is copied into LDS while the current one is computed.
+//  * With d = dv the normalised output leaves through LDS: each wave writes
+//    its 32 rows into one of the two K/V stages the item's last tile does
+//    not occupy and stores whole rows, 1 KiB contiguous per instruction.
 //  * The kernel is persistent: each workgroup walks units of two query
 //    blocks of one head whose causal costs add up to a constant, numbered
 //    so that workgroups of one XCD share heads (K/V reuse in that L2).
-//  * At d = 64 the kernel needs 80 KiB of LDS and about 125 registers, so
-//    two workgroups share a CU (the launch bounds ask for four waves per
-//    SIMD there).
-//    Their items start and end at different times, and one workgroup's
+//  * At d = 64 the kernel needs 80 KiB of LDS and 128 registers, so two
+//    workgroups share a CU (the launch bounds ask for four waves per SIMD
+//    there).  Their items start and end at different times, and one workgroup's
 //    item boundary (Q and first tiles in flight, output stores) overlaps
 //    the other's tile loop.  That wins over the one-workgroup ping-pong
 //    kernel of fa_fwd_mfma.hip while items are short (up to about 48 key
