@@ -37,9 +37,11 @@
 //    and XOR-swizzled per row (16-byte chunks for K, 64-byte groups for V)
 //    so that the operand reads are free of bank conflicts.  The Q block of
 //    the next item is copied into LDS while the current one is computed.
-//  * With d = dv the normalised output leaves through LDS: each wave writes
-//    its 32 rows into one of the two K/V stages the item's last tile does
-//    not occupy and stores whole rows, 1 KiB contiguous per instruction.
+//  * The normalised output leaves through LDS: each wave writes its 32 rows
+//    into one of the two K/V stages the item's last tile does not occupy
+//    and stores whole rows, 1 KiB contiguous per instruction (with d = 64
+//    and dv = 128 the stages hold six waves' rows; the other two store
+//    their registers directly).
 //  * The kernel is persistent: each workgroup walks units of two query
 //    blocks of one head whose causal costs add up to a constant, numbered
 //    so that workgroups of one XCD share heads (K/V reuse in that L2).
@@ -532,7 +534,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const auto ors = make_rsrc(o + (int64_t)head * N * DV, (uint32_t)N * DV * 2u);
         typedef T t4 __attribute__((ext_vector_type(4)));
-        if constexpr (D == DV) {
+        // (d = 64 with dv = 128: the two free stages hold six waves' blocks,
+        // two per V tile and one per K tile; waves 6 and 7 store directly)
+        if (D == DV || wave < 6) {
             // The wave's 32 x dv block goes through LDS and leaves as whole
             // rows (16 bytes per lane, 1 KiB contiguous per instruction).
             // Once every wave has passed the item's last barrier, only the
@@ -543,8 +547,16 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
             constexpr int RB = DV * 2;            // bytes per output row
             constexpr int CPRO = RB / 16;         // 16-byte chunks per row
             constexpr int RPI = 64 / CPRO;        // rows per store instruction
-            const int sidx = wave < 4 ? st : (st == 2 ? 0 : st + 1);
-            unsigned char *slot = ((wave / 2) % 2 == 0 ? kbuf[sidx] : vbuf[sidx]) + (wave % 2) * (kQW * RB);
+            const int st1 = st == 2 ? 0 : st + 1;
+            unsigned char *slot;
+            if constexpr (D == DV) {
+                const int sidx = wave < 4 ? st : st1;
+                slot = ((wave / 2) % 2 == 0 ? kbuf[sidx] : vbuf[sidx]) + (wave % 2) * (kQW * RB);
+            } else {
+                static_assert(TILEV == 2 * kQW * RB && TILE == kQW * RB, "six staged blocks");
+                slot = wave < 4 ? vbuf[wave < 2 ? st : st1] + (wave % 2) * (kQW * RB)
+                                : kbuf[wave == 4 ? st : st1];
+            }
             auto oswz = [](int r) __attribute__((always_inline)) {
                 return DV == 64 ? (r >> 1) & 7 : r & 15;
             };
