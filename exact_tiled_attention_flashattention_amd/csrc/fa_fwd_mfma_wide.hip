@@ -251,14 +251,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
         }
         issued += LPQ;
     };
-    // An item's first tiles: K and V tiles 0 and 1.
+    // An item's first tiles, K and V tiles 0 and 1, tile 0 first; `t1mark`
+    // is the count once tile 0 is issued.
+    int t1mark = 0;
     auto first_tiles = [&](int head, int ntiles) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < KLEAD; ++t)
-            if (t < ntiles) dma_k(head, t, t);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            if (t < ntiles) dma_v(head, t, t);
+        if (ntiles > 0) {
+            dma_k(head, 0, 0);
+            dma_v(head, 0, 0);
+        }
+        t1mark = issued;
+        if (ntiles > 1) {
+            dma_k(head, 1, 1);
+            dma_v(head, 1, 1);
+        }
     };
     auto barrier = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
@@ -386,15 +391,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
     // j-1 (`mark`) is outstanding; after the barrier (all reads of iteration
     // j-1 done) it fetches K and V tile j + 2 into the stage those reads
     // freed, so a tile is fetched two iterations before it is read.  An
-    // item's first two tiles are fetched once the previous item's reads are
-    // over, its Q block already during the previous item; both are waited
-    // for at the item's start (`pro_mark`).
+    // item's first two tiles (tile 0 first) are fetched once the previous
+    // item's reads are over, its Q block already during the previous item;
+    // the item's start waits for the Q block and tile 0 (`t1mark`), and
+    // iteration 0 for nothing more.
     Cursor cur = first_item(sch);
     if (cur.head >= 0 && !kSerialCopies) {
         dma_q(cur.head, cur.qblk);
         first_tiles(cur.head, cur.ntiles);
     }
-    int pro_mark = issued;
     bool first = true;
 
     typedef std::integral_constant<int, 0> I0;
@@ -427,7 +432,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
         if (!first && !kSerialCopies) {
             barrier();
             first_tiles(head, ntiles);
-            pro_mark = issued;
         }
         first = false;
         // This item's Q block and first tiles have landed everywhere.
@@ -436,7 +440,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
             dma_q(head, cur.qblk);
             wait_pending(0);
         } else {
-            wait_pending(issued - pro_mark);
+            const int pend = issued - t1mark;
+            if (pend == LPT + LPTV) wait_vmcnt<LPT + LPTV>();
+            else wait_pending(pend);
         }
         barrier();
 #pragma unroll
@@ -453,7 +459,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
             int hd = nxt.head, qb = nxt.qblk;
             asm volatile("" : "+s"(hd), "+s"(qb));
             if (hd >= 0) dma_q(hd, qb);
-            pro_mark = issued;
         };
         if (ntiles == 0 && !kSerialCopies) {
             barrier();
@@ -472,9 +477,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && DV == 64) ? 4 : 2) void fwd_m
             }
             // In the steady state the previous iteration issued exactly one
             // K and one V tile: that count gets its own short path.
-            const int pend = issued - mark;
-            if (pend == LPT + LPTV) wait_vmcnt<LPT + LPTV>();
-            else wait_pending(pend);
+            if (j > 0) {
+                const int pend = issued - mark;
+                if (pend == LPT + LPTV) wait_vmcnt<LPT + LPTV>();
+                else wait_pending(pend);
+            }
             barrier();
             mark = issued;
             static_assert(KLEAD == 2, "stage two ahead");
