@@ -109,33 +109,28 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes) {
 // Issued as inline assembly so that the compiler does not track it: the
 // caller waits for it (s_waitcnt vmcnt) and publishes it (s_barrier) itself.
 // Out-of-range offsets write zeros.  `lds_addr` must be wave-uniform.
-// The LDS address travels in M0, which the compiler reserves: the sequence
-// saves and restores it, and keeps the one wait state the ISA asks for
-// between a scalar write of M0 and an LDS-copying load.
+// The LDS address travels in M0, declared clobbered so that the compiler
+// saves it only where it holds a live value there; the sequence keeps the
+// one wait state the ISA asks for between a scalar write of M0 and an
+// LDS-copying load.
 __device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %1\n\t"
+    asm volatile("s_mov_b32 m0, %0\n\t"
                  "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved)
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // The same copy with 4 bytes per lane (buffer_load_dword ... lds): lane i's
 // word lands at lds_addr + 4 i.
 __device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %1\n\t"
+    asm volatile("s_mov_b32 m0, %0\n\t"
                  "s_nop 0\n\t"
-                 "buffer_load_dword %2, %3, 0 offen lds\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved)
+                 "buffer_load_dword %1, %2, 0 offen lds"
+                 :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Stores a wave's 16 x W result tile (W = D or DV columns) as whole rows.
